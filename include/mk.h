@@ -1,0 +1,203 @@
+/*
+ * mk.h -- C ABI of the MI355X (gfx950) low-latency decode megakernel.
+ *
+ * One call, mk_decode_step, runs the whole batch-1 decode forward pass of a
+ * Llama-style decoder (pre-norm, GQA attention with RoPE, SwiGLU FFN, RMSNorm,
+ * tied or untied LM head, greedy argmax) as ONE persistent GPU kernel: every
+ * workgroup stays resident on its compute unit, walks a host-planned task tape
+ * and waits on flags in device memory instead of on kernel boundaries.
+ *
+ * Source of the operations: the pages "Revolution der KI-Beschleunigung: Wie
+ * ein Low-Latency Megakernel den Llama-1B Turbo zuendet" (dasgeld.co) and the
+ * glossary entry "Megakernel" (synthszr.com).  The article describes fusing all
+ * steps of the Llama-1B bf16 forward pass into one kernel, an instruction
+ * interpreter fed with sequences planned once on the host and reused for every
+ * forward pass, dependency tracking through global counters in GPU memory, and
+ * a paged shared memory that lets the next load start while another finishes.
+ * The glossary section "Wie eine ganze Rechenkette in ein Programm passt" adds
+ * that the kernel is started once and takes its tasks from a work list, and
+ * that counters and signals in memory replace host control between launches.
+ * The pages give no API and no model formulas; the calls below follow the
+ * problem as the pages state it (per-token decode with a reusable host plan)
+ * and the model is the textbook Llama-style decoder.
+ *
+ * Conventions for every call:
+ *   - return 0 (MK_OK) on success, a negative MK_E_* code on failure;
+ *   - pointers marked "device" must be device memory of the current HIP device;
+ *   - bf16 tensors are passed as uint16_t bit patterns;
+ *   - matrices are row-major [out][in];
+ *   - the library never frees memory it did not allocate.
+ */
+#ifndef MK_H_
+#define MK_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Error codes. */
+#define MK_OK 0
+#define MK_E_INVAL (-1)       /* null, misaligned or inconsistent argument        */
+#define MK_E_RANGE (-2)       /* position outside [0, max_seq)                     */
+#define MK_E_HIP (-3)         /* a HIP runtime call failed                         */
+#define MK_E_STATE (-4)       /* a device error is latched; call mk_reset          */
+#define MK_E_TIMEOUT (-5)     /* a dependency wait exceeded the watchdog budget    */
+#define MK_E_TOKEN (-6)       /* an input token id was outside [0, vocab)          */
+#define MK_E_NOMEM (-7)       /* device or host allocation failed                  */
+#define MK_E_UNSUPPORTED (-8) /* configuration not supported by this build         */
+#define MK_E_DEVICE (-9)      /* device does not fit the persistent launch         */
+
+/* Execution modes of mk_decode_step. */
+#define MK_MODE_MEGA 0  /* one persistent kernel per decode step                 */
+#define MK_MODE_MULTI 1 /* one kernel launch per stage (the bubble baseline)     */
+#define MK_MODE_GRAPH 2 /* the MULTI launches captured once into a hipGraph      */
+
+/* Model and run configuration.
+ * Llama-style decoder: n_layers, hidden H, n_heads query heads and n_kv_heads
+ * key/value heads of head_dim each (n_heads % n_kv_heads == 0, head_dim even),
+ * SwiGLU width ffn, vocabulary vocab.  max_seq bounds the positions and is
+ * the slot count of the caller's KV cache; batch is the number of independent
+ * sequences decoded per step (1 in this build).  rms_eps and rope_theta are
+ * the RMSNorm epsilon and the RoPE base.  tie_embeddings != 0 uses the
+ * embedding matrix as LM head.  exec_mode is one of MK_MODE_*.
+ * attn_chunks: split of [0, pos] per KV head in attention (0 = automatic).
+ * num_wgs: persistent workgroups (0 = one per compute unit).
+ * watchdog_ms: budget of any single dependency wait (0 = 2000 ms). */
+typedef struct mk_config {
+  int32_t n_layers;
+  int32_t hidden;
+  int32_t n_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t ffn;
+  int32_t vocab;
+  int32_t max_seq;
+  int32_t batch;
+  float rms_eps;
+  double rope_theta;
+  int32_t tie_embeddings;
+  int32_t exec_mode;
+  int32_t attn_chunks;
+  int32_t num_wgs;
+  int32_t watchdog_ms;
+  int32_t reserved[7];
+} mk_config;
+
+/* Device pointers to one layer's bf16 weights (row-major [out][in]):
+ * attn_norm[H], wq[n_heads*head_dim][H], wk[n_kv_heads*head_dim][H],
+ * wv[n_kv_heads*head_dim][H], wo[H][n_heads*head_dim], ffn_norm[H],
+ * w_gate[ffn][H], w_up[ffn][H], w_down[H][ffn]. */
+typedef struct mk_layer_weights {
+  const uint16_t* attn_norm;
+  const uint16_t* wq;
+  const uint16_t* wk;
+  const uint16_t* wv;
+  const uint16_t* wo;
+  const uint16_t* ffn_norm;
+  const uint16_t* w_gate;
+  const uint16_t* w_up;
+  const uint16_t* w_down;
+} mk_layer_weights;
+
+/* Model weights: device pointers embed[vocab][H], final_norm[H], lm_head
+ * [vocab][H] (NULL iff tie_embeddings), and a HOST array of n_layers
+ * mk_layer_weights.  mk_load copies every layer matrix into a library-owned
+ * packed layout.  embed is read in place (the first layer gathers its rows),
+ * and so is the LM head (embed when tied, else lm_head) when hidden is a
+ * multiple of 512 and needs no row padding: those buffers must stay valid
+ * until mk_free; all others may be released once mk_load returns. */
+typedef struct mk_weights {
+  const uint16_t* embed;
+  const uint16_t* final_norm;
+  const uint16_t* lm_head;
+  const mk_layer_weights* layers;
+} mk_weights;
+
+/* Caller-owned bf16 KV cache, device memory, layout
+ * [batch][n_layers][n_kv_heads][max_seq][head_dim] for K and for V.
+ * Keys are stored after the rotary embedding.  Both may be NULL when
+ * n_layers == 0. */
+typedef struct mk_kv {
+  uint16_t* k;
+  uint16_t* v;
+} mk_kv;
+
+/* Latched device status.  code is MK_OK or the first device error;
+ * task/stage/wg locate a watchdog timeout, detail holds the bad token id
+ * or the value the wait last observed. */
+typedef struct mk_status_t {
+  int32_t code;
+  int32_t stage;
+  int32_t wg;
+  uint32_t detail;
+} mk_status_t;
+
+/* Plan summary (host only; see mk_plan_describe). */
+typedef struct mk_plan_info {
+  int32_t num_wgs;        /* persistent workgroups                          */
+  int32_t num_stages;     /* stages on the tape (5 per layer + LM head)     */
+  int32_t num_tasks;      /* non-empty (stage, workgroup) entries           */
+  int32_t attn_chunks;    /* KV split per head used by attention            */
+  int64_t weight_bytes;   /* bytes of the packed weight arena               */
+  int64_t workspace_bytes;/* bytes of activations, flags, tape, tables      */
+  int32_t lds_bytes;      /* dynamic LDS per workgroup                      */
+  int32_t reserved[5];
+} mk_plan_info;
+
+typedef struct mk_handle mk_handle;
+
+/* mk_load -- validate cfg, pack the weights, build the task tape, allocate the
+ * workspace, and return a handle in *out.
+ * The tape splits every matrix op of every layer into row tiles, one tile per
+ * workgroup and stage (the article's instruction sequences planned on the host
+ * once and reused for every forward pass).  All device work runs on the null
+ * stream and is complete on return.
+ * Errors: MK_E_INVAL (bad cfg/pointers), MK_E_UNSUPPORTED, MK_E_DEVICE,
+ * MK_E_NOMEM, MK_E_HIP.  On error *out is NULL and nothing leaks. */
+int mk_load(const mk_config* cfg, const mk_weights* w, mk_handle** out);
+
+/* mk_decode_step -- one decode step at position pos for every sequence.
+ * d_token[batch] (device int32) holds the input token ids; the previous
+ * step's out_token may be passed directly.  kv is the caller's cache: slot
+ * pos of every (sequence, layer, kv head) is written, slots [0, pos] are read,
+ * slots above pos are never touched.  out_logits[batch][vocab] (device fp32)
+ * and out_token[batch] (device int32, first index of the maximum logit) are
+ * written.  Asynchronous on stream; allocates nothing and never synchronises.
+ * Synchronous errors: MK_E_INVAL, MK_E_RANGE, MK_E_STATE (an earlier step
+ * latched a device error: see mk_status), MK_E_HIP.  A device-side bad token
+ * latches MK_E_TOKEN and writes out_token = -1; a wait that exceeds the
+ * watchdog latches MK_E_TIMEOUT and ends the kernel early.
+ * One handle must not be used from two streams or threads at once. */
+int mk_decode_step(mk_handle* h, const int32_t* d_token, int32_t pos, const mk_kv* kv,
+                   float* out_logits, int32_t* out_token, hipStream_t stream);
+
+/* mk_reset -- wait for the handle's last stream, clear every flag, counter and
+ * latched error and restart the step count.  Weights and the caller's cache
+ * are untouched; a new sequence simply starts at pos = 0. */
+int mk_reset(mk_handle* h);
+
+/* mk_free -- wait for outstanding work and release everything the handle owns. */
+void mk_free(mk_handle* h);
+
+/* mk_status -- copy the latched device status (no synchronisation). */
+int mk_status(mk_handle* h, mk_status_t* out);
+
+/* mk_error_string -- static text for an MK_* code. */
+const char* mk_error_string(int code);
+
+/* mk_plan_describe -- build and validate the task tape for cfg on num_wgs
+ * workgroups (0 = assume 256) on the HOST ONLY, without touching a GPU, and
+ * fill *out.  Returns MK_OK if the tape passes the validator: stages in
+ * dependency order, every row pair of every matrix covered exactly once,
+ * every (kv head, chunk) attention task present once, LDS and scratch
+ * bounds respected. */
+int mk_plan_describe(const mk_config* cfg, int32_t num_wgs, mk_plan_info* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MK_H_ */

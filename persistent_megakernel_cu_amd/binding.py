@@ -1,0 +1,215 @@
+"""ctypes binding of libmk.so (include/mk.h): argument marshalling only.
+
+Every step of the decode path runs in the HIP kernels behind the C ABI;
+PyTorch only provides device memory and the stream handle.  Importing this
+module does not touch a GPU; creating an Engine does.  A missing library is
+an error, never a fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmk.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "mk.h")
+
+MK_OK = 0
+MK_E_INVAL = -1
+MK_E_RANGE = -2
+MK_E_HIP = -3
+MK_E_STATE = -4
+MK_E_TIMEOUT = -5
+MK_E_TOKEN = -6
+MK_E_NOMEM = -7
+MK_E_UNSUPPORTED = -8
+MK_E_DEVICE = -9
+
+MODE_MEGA = 0
+MODE_MULTI = 1
+MODE_GRAPH = 2
+MODES = {"mega": MODE_MEGA, "multi": MODE_MULTI, "graph": MODE_GRAPH}
+
+
+class MkConfig(ctypes.Structure):
+    _fields_ = [
+        ("n_layers", ctypes.c_int32), ("hidden", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("ffn", ctypes.c_int32),
+        ("vocab", ctypes.c_int32), ("max_seq", ctypes.c_int32), ("batch", ctypes.c_int32),
+        ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_double), ("tie_embeddings", ctypes.c_int32),
+        ("exec_mode", ctypes.c_int32), ("attn_chunks", ctypes.c_int32), ("num_wgs", ctypes.c_int32),
+        ("watchdog_ms", ctypes.c_int32), ("reserved", ctypes.c_int32 * 7),
+    ]
+
+
+class MkLayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down")]
+
+
+class MkWeights(ctypes.Structure):
+    _fields_ = [("embed", ctypes.c_void_p), ("final_norm", ctypes.c_void_p), ("lm_head", ctypes.c_void_p),
+                ("layers", ctypes.POINTER(MkLayerWeights))]
+
+
+class MkKv(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p)]
+
+
+class MkStatus(ctypes.Structure):
+    _fields_ = [("code", ctypes.c_int32), ("stage", ctypes.c_int32), ("wg", ctypes.c_int32),
+                ("detail", ctypes.c_uint32)]
+
+
+class MkPlanInfo(ctypes.Structure):
+    _fields_ = [("num_wgs", ctypes.c_int32), ("num_stages", ctypes.c_int32), ("num_tasks", ctypes.c_int32),
+                ("attn_chunks", ctypes.c_int32), ("weight_bytes", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_int64), ("lds_bytes", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 5)]
+
+
+class MkError(RuntimeError):
+    def __init__(self, code: int, what: str = ""):
+        self.code = code
+        super().__init__(f"{what}: {error_string(code)} ({code})" if what else f"{error_string(code)} ({code})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmk.so (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: run `python -m persistent_megakernel_cu_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.mk_load.argtypes = [ctypes.POINTER(MkConfig), ctypes.POINTER(MkWeights), ctypes.POINTER(ctypes.c_void_p)]
+        L.mk_load.restype = ctypes.c_int
+        L.mk_decode_step.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(MkKv),
+                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.mk_decode_step.restype = ctypes.c_int
+        L.mk_reset.argtypes = [ctypes.c_void_p]
+        L.mk_reset.restype = ctypes.c_int
+        L.mk_free.argtypes = [ctypes.c_void_p]
+        L.mk_free.restype = None
+        L.mk_status.argtypes = [ctypes.c_void_p, ctypes.POINTER(MkStatus)]
+        L.mk_status.restype = ctypes.c_int
+        L.mk_error_string.argtypes = [ctypes.c_int]
+        L.mk_error_string.restype = ctypes.c_char_p
+        L.mk_plan_describe.argtypes = [ctypes.POINTER(MkConfig), ctypes.c_int32, ctypes.POINTER(MkPlanInfo)]
+        L.mk_plan_describe.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/mk.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_\s\*]*?\b(mk_[a-z_]+)\s*\(", text, re.M)))
+
+
+def error_string(code: int) -> str:
+    return lib().mk_error_string(int(code)).decode()
+
+
+def make_config(shape, max_seq: int, batch: int = 1, mode: str | int = "mega", attn_chunks: int = 0,
+                num_wgs: int = 0, watchdog_ms: int = 0) -> MkConfig:
+    c = MkConfig()
+    c.n_layers, c.hidden, c.n_heads = shape.n_layers, shape.hidden, shape.n_heads
+    c.n_kv_heads, c.head_dim, c.ffn, c.vocab = shape.n_kv_heads, shape.head_dim, shape.ffn, shape.vocab
+    c.max_seq, c.batch = max_seq, batch
+    c.rms_eps, c.rope_theta = shape.rms_eps, shape.rope_theta
+    c.tie_embeddings = 1 if shape.tie_embeddings else 0
+    c.exec_mode = MODES[mode] if isinstance(mode, str) else int(mode)
+    c.attn_chunks, c.num_wgs, c.watchdog_ms = attn_chunks, num_wgs, watchdog_ms
+    return c
+
+
+def plan_describe(shape, max_seq: int, num_wgs: int = 256, **kw) -> MkPlanInfo:
+    """Build and validate the task tape on the host (no GPU needed)."""
+    info = MkPlanInfo()
+    rc = lib().mk_plan_describe(ctypes.byref(make_config(shape, max_seq, **kw)), num_wgs, ctypes.byref(info))
+    if rc != MK_OK:
+        raise MkError(rc, "mk_plan_describe")
+    return info
+
+
+class Engine:
+    """One mk_handle: weights loaded once, then one decode step per call.
+
+    ``weights`` maps tensor names (see synth_inputs.weight_shapes) to device
+    tensors holding bf16 bit patterns (int16/uint16/bfloat16 dtype).  Only the
+    embedding must stay alive; the engine keeps a reference to it.
+    """
+
+    def __init__(self, shape, weights: dict, max_seq: int, mode: str = "mega", batch: int = 1,
+                 attn_chunks: int = 0, num_wgs: int = 0, watchdog_ms: int = 0):
+        self.shape = shape
+        self.max_seq = max_seq
+        self.batch = batch
+        self.cfg = make_config(shape, max_seq, batch, mode, attn_chunks, num_wgs, watchdog_ms)
+        ptr = lambda name: ctypes.c_void_p(weights[name].data_ptr())
+        layers = (MkLayerWeights * max(1, shape.n_layers))()
+        for l in range(shape.n_layers):
+            for f in MkLayerWeights._fields_:
+                setattr(layers[l], f[0], weights[f"layers.{l}.{f[0]}"].data_ptr())
+        w = MkWeights()
+        w.embed = weights["embed"].data_ptr()
+        w.final_norm = weights["final_norm"].data_ptr()
+        w.lm_head = weights["lm_head"].data_ptr() if not shape.tie_embeddings else None
+        w.layers = layers
+        del ptr
+        self._embed = weights["embed"]
+        h = ctypes.c_void_p()
+        rc = lib().mk_load(ctypes.byref(self.cfg), ctypes.byref(w), ctypes.byref(h))
+        if rc != MK_OK:
+            raise MkError(rc, "mk_load")
+        self._h = h
+        self._kv = MkKv()
+
+    def decode_step(self, token, pos: int, kcache, vcache, logits, out_token, stream=None) -> None:
+        """Enqueue one step on ``stream`` (a torch.cuda.Stream or raw handle; default: current)."""
+        if stream is None:
+            import torch
+            stream = torch.cuda.current_stream().cuda_stream
+        elif hasattr(stream, "cuda_stream"):
+            stream = stream.cuda_stream
+        self._kv.k = kcache.data_ptr()
+        self._kv.v = vcache.data_ptr()
+        rc = lib().mk_decode_step(self._h, token.data_ptr(), int(pos), ctypes.byref(self._kv), logits.data_ptr(),
+                                  out_token.data_ptr(), ctypes.c_void_p(stream))
+        if rc != MK_OK:
+            raise MkError(rc, "mk_decode_step")
+
+    def status(self) -> MkStatus:
+        s = MkStatus()
+        lib().mk_status(self._h, ctypes.byref(s))
+        return s
+
+    def reset(self) -> None:
+        rc = lib().mk_reset(self._h)
+        if rc != MK_OK:
+            raise MkError(rc, "mk_reset")
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            lib().mk_free(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def to_device(weights_np: dict, device="cuda") -> dict:
+    """Copy uint16 bf16 bit arrays to device int16 tensors (bit-identical)."""
+    import torch
+    out = {}
+    for k, a in weights_np.items():
+        out[k] = torch.from_numpy(a.view("int16")).to(device)
+    return out

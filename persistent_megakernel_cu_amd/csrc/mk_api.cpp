@@ -1,0 +1,445 @@
+// mk_api.cpp -- the C ABI (include/mk.h): load, decode step, reset, status.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/mk.h"
+#include "mk_internal.h"
+#include "mk_plan.h"
+
+namespace mk {
+hipError_t configure_kernels(int lds_bytes);
+hipError_t persistent_occupancy(int lds_bytes, int* blocks_per_cu);
+hipError_t launch_persistent(const Params& P, int lds_bytes, hipStream_t stream);
+hipError_t launch_stage(const Params& P, int s, int lds_bytes, hipStream_t stream);
+hipError_t launch_set_args(StepArgs* a, int pos, uint32_t epoch, hipStream_t stream);
+hipError_t launch_advance_args(StepArgs* a, hipStream_t stream);
+}  // namespace mk
+
+using mk::Params;
+using mk::Plan;
+
+namespace {
+
+// Step tags restart (with a workspace clear) before epoch * tasks-per-stage could wrap a u32.
+constexpr uint32_t kEpochLimit = 1u << 20;
+
+struct Workspace {
+  size_t x_attn, x_ffn, q, kvcur, o, h, attn_part, attn_ctr, amax, amax_ctr, tokerr, abort_flag, status, dargs;
+  size_t bytes;
+};
+
+size_t take(size_t& cur, size_t bytes) {
+  size_t at = cur;
+  cur = (cur + bytes + 255) / 256 * 256;
+  return at;
+}
+
+Workspace layout_workspace(const Plan& p) {
+  Workspace w{};
+  size_t cur = 0;
+  const size_t L = std::max(p.L, 1), B = p.B;
+  w.x_attn = take(cur, B * L * p.H * 8);
+  w.x_ffn = take(cur, B * L * p.H * 8);
+  w.q = take(cur, B * L * p.QD * 8);
+  w.kvcur = take(cur, B * L * 2 * p.KVD * 8);
+  w.o = take(cur, B * L * p.QD * 8);
+  w.h = take(cur, B * L * p.F * 8);
+  w.attn_part = take(cur, B * L * p.NKV * p.C * p.G * (p.D + 2) * 4);
+  w.attn_ctr = take(cur, B * L * p.NKV * 4);
+  w.amax = take(cur, B * p.W * 8);
+  w.amax_ctr = take(cur, B * 4);
+  w.tokerr = take(cur, B * 4);
+  w.abort_flag = take(cur, 4);
+  w.status = take(cur, sizeof(mk::DevStatus));
+  w.dargs = take(cur, sizeof(mk::StepArgs));
+  w.bytes = cur;
+  return w;
+}
+
+}  // namespace
+
+struct mk_handle {
+  mk_config cfg{};
+  Plan plan;
+  int device = 0;
+  char* arena = nullptr;
+  char* lm_copy = nullptr;
+  const char* lm = nullptr;
+  const uint16_t* embed = nullptr;
+  float* gains = nullptr;  // g_attn [L][Hp] | g_ffn [L][Hp] | g_final [Hp]
+  float* rope = nullptr;
+  mk::Task* tape = nullptr;
+  char* ws = nullptr;
+  Workspace wl{};
+  mk::DevStatus* status_host = nullptr;     // pinned, host-mapped
+  mk::DevStatus* status_host_dev = nullptr; // its device address
+  hipStream_t capture_stream = nullptr;
+  hipStream_t last_stream = nullptr;
+  bool used = false;
+  uint32_t epoch = 0;
+  uint64_t watchdog_ticks = 0;
+  // graph mode
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t gexec = nullptr;
+  const void* g_ptrs[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
+  int shadow_pos = -1;
+  uint32_t shadow_epoch = 0;
+};
+
+namespace {
+
+void release(mk_handle* h) {
+  if (!h) return;
+  if (h->gexec) (void)hipGraphExecDestroy(h->gexec);
+  if (h->graph) (void)hipGraphDestroy(h->graph);
+  if (h->capture_stream) (void)hipStreamDestroy(h->capture_stream);
+  if (h->arena) (void)hipFree(h->arena);
+  if (h->lm_copy) (void)hipFree(h->lm_copy);
+  if (h->gains) (void)hipFree(h->gains);
+  if (h->rope) (void)hipFree(h->rope);
+  if (h->tape) (void)hipFree(h->tape);
+  if (h->ws) (void)hipFree(h->ws);
+  if (h->status_host) (void)hipHostFree(h->status_host);
+  delete h;
+}
+
+Params make_params(mk_handle* h) {
+  const Plan& p = h->plan;
+  Params P{};
+  P.tape = h->tape;
+  P.num_wgs = p.W;
+  P.num_stages = p.stages;
+  P.L = p.L; P.H = p.H; P.Hp = p.Hp; P.QD = p.QD; P.QDp = p.QDp; P.KVD = p.KVD;
+  P.F = p.F; P.Fp = p.Fp; P.V = p.V; P.NQ = p.NQ; P.NKV = p.NKV; P.D = p.D; P.G = p.G; P.S = p.S; P.B = p.B;
+  P.eps = h->cfg.rms_eps;
+  P.qscale = (float)(1.0 / std::sqrt((double)p.D));
+  P.attn_chunks = p.C;
+  P.arena = h->arena;
+  P.lm = h->lm;
+  P.embed = h->embed;
+  P.g_attn = h->gains;
+  P.g_ffn = h->gains + (size_t)p.L * p.Hp;
+  P.g_final = h->gains + 2 * (size_t)p.L * p.Hp;
+  P.rope = h->rope;
+  char* ws = h->ws;
+  const Workspace& w = h->wl;
+  P.x_attn = reinterpret_cast<uint64_t*>(ws + w.x_attn);
+  P.x_ffn = reinterpret_cast<uint64_t*>(ws + w.x_ffn);
+  P.q = reinterpret_cast<uint64_t*>(ws + w.q);
+  P.kvcur = reinterpret_cast<uint64_t*>(ws + w.kvcur);
+  P.o = reinterpret_cast<uint64_t*>(ws + w.o);
+  P.h = reinterpret_cast<uint64_t*>(ws + w.h);
+  P.attn_part = reinterpret_cast<float*>(ws + w.attn_part);
+  P.attn_ctr = reinterpret_cast<uint32_t*>(ws + w.attn_ctr);
+  P.amax = reinterpret_cast<uint64_t*>(ws + w.amax);
+  P.amax_ctr = reinterpret_cast<uint32_t*>(ws + w.amax_ctr);
+  P.tokerr = reinterpret_cast<uint32_t*>(ws + w.tokerr);
+  P.abort_flag = reinterpret_cast<uint32_t*>(ws + w.abort_flag);
+  P.status = reinterpret_cast<mk::DevStatus*>(ws + w.status);
+  P.status_host = h->status_host_dev;
+  P.lds_act = p.lds_act;
+  P.lds_res = p.lds_res;
+  P.lds_rope = p.lds_rope;
+  P.lds_misc = p.lds_misc;
+  P.act_floats = p.act_floats;
+  P.res_floats = p.res_floats;
+  P.watchdog_ticks = h->watchdog_ticks;
+  return P;
+}
+
+#define HIP_OR(call)                  \
+  do {                                \
+    if ((call) != hipSuccess) {       \
+      (void)hipGetLastError();        \
+      release(h);                     \
+      return MK_E_HIP;                \
+    }                                 \
+  } while (0)
+
+// bf16 gains (device) -> fp32 zero-padded rows (host staging)
+bool widen_gain(const uint16_t* dsrc, int n, float* hdst) {
+  std::vector<uint16_t> tmp(n);
+  if (hipMemcpy(tmp.data(), dsrc, (size_t)n * 2, hipMemcpyDeviceToHost) != hipSuccess) return false;
+  for (int i = 0; i < n; ++i) {
+    uint32_t u = (uint32_t)tmp[i] << 16;
+    std::memcpy(&hdst[i], &u, 4);
+  }
+  return true;
+}
+
+int clear_workspace(mk_handle* h, hipStream_t s) {
+  if (hipMemsetAsync(h->ws, 0, h->wl.bytes, s) != hipSuccess) return MK_E_HIP;
+  return MK_OK;
+}
+
+int capture_graph(mk_handle* h, const Params& base) {
+  if (h->gexec) { (void)hipGraphExecDestroy(h->gexec); h->gexec = nullptr; }
+  if (h->graph) { (void)hipGraphDestroy(h->graph); h->graph = nullptr; }
+  Params P = base;
+  P.dargs = reinterpret_cast<mk::StepArgs*>(h->ws + h->wl.dargs);
+  hipStream_t cs = h->capture_stream;
+  if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) return MK_E_HIP;
+  bool ok = true;
+  for (int s = 0; s < h->plan.stages && ok; ++s) ok = mk::launch_stage(P, s, h->plan.lds_bytes, cs) == hipSuccess;
+  if (ok) ok = mk::launch_advance_args(const_cast<mk::StepArgs*>(P.dargs), cs) == hipSuccess;
+  hipGraph_t g = nullptr;
+  hipError_t e = hipStreamEndCapture(cs, &g);
+  if (!ok || e != hipSuccess || !g) {
+    if (g) (void)hipGraphDestroy(g);
+    (void)hipGetLastError();
+    return MK_E_HIP;
+  }
+  if (hipGraphInstantiate(&h->gexec, g, nullptr, nullptr, 0) != hipSuccess) {
+    (void)hipGraphDestroy(g);
+    h->gexec = nullptr;
+    return MK_E_HIP;
+  }
+  h->graph = g;
+  h->shadow_pos = -1;
+  return MK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mk_error_string(int code) {
+  switch (code) {
+    case MK_OK: return "ok";
+    case MK_E_INVAL: return "invalid argument";
+    case MK_E_RANGE: return "position out of range";
+    case MK_E_HIP: return "HIP runtime error";
+    case MK_E_STATE: return "a device error is latched (see mk_status; call mk_reset)";
+    case MK_E_TIMEOUT: return "dependency wait exceeded the watchdog budget";
+    case MK_E_TOKEN: return "input token id out of range";
+    case MK_E_NOMEM: return "out of memory";
+    case MK_E_UNSUPPORTED: return "configuration not supported";
+    case MK_E_DEVICE: return "device cannot host the persistent launch";
+    default: return "unknown error";
+  }
+}
+
+int mk_plan_describe(const mk_config* cfg, int32_t num_wgs, mk_plan_info* out) {
+  if (!cfg || !out) return MK_E_INVAL;
+  Plan p;
+  int rc = mk::plan_build(*cfg, num_wgs > 0 ? num_wgs : 256, p);
+  if (rc != MK_OK) return rc;
+  std::string why;
+  rc = mk::plan_validate(p, &why);
+  if (rc != MK_OK) return rc;
+  std::memset(out, 0, sizeof(*out));
+  out->num_wgs = p.W;
+  out->num_stages = p.stages;
+  out->num_tasks = p.num_tasks;
+  out->attn_chunks = p.C;
+  out->weight_bytes = (int64_t)(p.arena_bytes + p.lm_bytes);
+  out->workspace_bytes = (int64_t)layout_workspace(p).bytes + (int64_t)p.tape.size() * 32;
+  out->lds_bytes = p.lds_bytes;
+  return MK_OK;
+}
+
+int mk_load(const mk_config* cfg, const mk_weights* w, mk_handle** out) {
+  if (out) *out = nullptr;
+  if (!cfg || !w || !out || !w->embed || !w->final_norm) return MK_E_INVAL;
+  if ((cfg->tie_embeddings != 0) != (w->lm_head == nullptr)) return MK_E_INVAL;
+  if (cfg->n_layers > 0 && !w->layers) return MK_E_INVAL;
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const mk_layer_weights& lw = w->layers[l];
+    if (!lw.attn_norm || !lw.wq || !lw.wk || !lw.wv || !lw.wo || !lw.ffn_norm || !lw.w_gate || !lw.w_up || !lw.w_down)
+      return MK_E_INVAL;
+  }
+  mk_handle* h = new (std::nothrow) mk_handle();
+  if (!h) return MK_E_NOMEM;
+  h->cfg = *cfg;
+  HIP_OR(hipGetDevice(&h->device));
+  hipDeviceProp_t prop;
+  HIP_OR(hipGetDeviceProperties(&prop, h->device));
+  const int ncu = prop.multiProcessorCount;
+  const int W = cfg->num_wgs > 0 ? cfg->num_wgs : ncu;
+  if (W > ncu) { release(h); return MK_E_DEVICE; }
+  int rc = mk::plan_build(*cfg, W, h->plan);
+  if (rc != MK_OK) { release(h); return rc; }
+  std::string why;
+  if (mk::plan_validate(h->plan, &why) != MK_OK) { release(h); return MK_E_INVAL; }
+  const Plan& p = h->plan;
+
+  // persistent residency: one workgroup per compute unit must fit
+  HIP_OR(mk::configure_kernels(p.lds_bytes));
+  int per_cu = 0;
+  HIP_OR(mk::persistent_occupancy(p.lds_bytes, &per_cu));
+  if (per_cu < 1) { release(h); return MK_E_DEVICE; }
+
+  // packed weights
+  if (hipMalloc(&h->arena, p.arena_bytes) != hipSuccess) { (void)hipGetLastError(); release(h); return MK_E_NOMEM; }
+  HIP_OR(hipMemset(h->arena, 0, p.arena_bytes));
+  const size_t H2 = (size_t)p.H * 2, Hp2 = (size_t)p.Hp * 2;
+  for (int l = 0; l < p.L; ++l) {
+    const mk_layer_weights& lw = w->layers[l];
+    char* q = h->arena + p.off_qkv[l];
+    HIP_OR(hipMemcpy2D(q, Hp2, lw.wq, H2, H2, p.QD, hipMemcpyDeviceToDevice));
+    HIP_OR(hipMemcpy2D(q + (size_t)p.QD * Hp2, Hp2, lw.wk, H2, H2, p.KVD, hipMemcpyDeviceToDevice));
+    HIP_OR(hipMemcpy2D(q + (size_t)(p.QD + p.KVD) * Hp2, Hp2, lw.wv, H2, H2, p.KVD, hipMemcpyDeviceToDevice));
+    HIP_OR(hipMemcpy2D(h->arena + p.off_o[l], (size_t)p.QDp * 2, lw.wo, (size_t)p.QD * 2, (size_t)p.QD * 2, p.H,
+                       hipMemcpyDeviceToDevice));
+    // gate row f -> packed row 2f, up row f -> packed row 2f+1
+    HIP_OR(hipMemcpy2D(h->arena + p.off_gu[l], 2 * Hp2, lw.w_gate, H2, H2, p.F, hipMemcpyDeviceToDevice));
+    HIP_OR(hipMemcpy2D(h->arena + p.off_gu[l] + Hp2, 2 * Hp2, lw.w_up, H2, H2, p.F, hipMemcpyDeviceToDevice));
+    HIP_OR(hipMemcpy2D(h->arena + p.off_down[l], (size_t)p.Fp * 2, lw.w_down, (size_t)p.F * 2, (size_t)p.F * 2, p.H,
+                       hipMemcpyDeviceToDevice));
+  }
+  const uint16_t* lm_src = p.tied ? w->embed : w->lm_head;
+  if (p.lm_borrowed) {
+    h->lm = reinterpret_cast<const char*>(lm_src);
+  } else {
+    if (hipMalloc(&h->lm_copy, p.lm_bytes) != hipSuccess) { (void)hipGetLastError(); release(h); return MK_E_NOMEM; }
+    HIP_OR(hipMemset(h->lm_copy, 0, p.lm_bytes));
+    HIP_OR(hipMemcpy2D(h->lm_copy, Hp2, lm_src, H2, H2, p.V, hipMemcpyDeviceToDevice));
+    h->lm = h->lm_copy;
+  }
+  h->embed = w->embed;
+
+  // norm gains as fp32, zero-padded to Hp
+  {
+    std::vector<float> g((size_t)(2 * p.L + 1) * p.Hp, 0.f);
+    for (int l = 0; l < p.L; ++l) {
+      if (!widen_gain(w->layers[l].attn_norm, p.H, &g[(size_t)l * p.Hp]) ||
+          !widen_gain(w->layers[l].ffn_norm, p.H, &g[(size_t)(p.L + l) * p.Hp])) {
+        release(h);
+        return MK_E_HIP;
+      }
+    }
+    if (!widen_gain(w->final_norm, p.H, &g[(size_t)2 * p.L * p.Hp])) { release(h); return MK_E_HIP; }
+    HIP_OR(hipMalloc(&h->gains, g.size() * 4));
+    HIP_OR(hipMemcpy(h->gains, g.data(), g.size() * 4, hipMemcpyHostToDevice));
+  }
+
+  // RoPE table: angle p * theta^(-2i/d_h) and its cos/sin in double, stored as float
+  {
+    std::vector<float> t((size_t)p.S * p.D);
+    for (int pos = 0; pos < p.S; ++pos)
+      for (int i = 0; i < p.D / 2; ++i) {
+        const double ang = (double)pos * std::pow(cfg->rope_theta, -2.0 * i / (double)p.D);
+        t[(size_t)pos * p.D + 2 * i] = (float)std::cos(ang);
+        t[(size_t)pos * p.D + 2 * i + 1] = (float)std::sin(ang);
+      }
+    HIP_OR(hipMalloc(&h->rope, t.size() * 4));
+    HIP_OR(hipMemcpy(h->rope, t.data(), t.size() * 4, hipMemcpyHostToDevice));
+  }
+
+  // tape
+  HIP_OR(hipMalloc(&h->tape, p.tape.size() * sizeof(mk::Task)));
+  HIP_OR(hipMemcpy(h->tape, p.tape.data(), p.tape.size() * sizeof(mk::Task), hipMemcpyHostToDevice));
+
+  // workspace
+  h->wl = layout_workspace(p);
+  if (hipMalloc(&h->ws, h->wl.bytes) != hipSuccess) { (void)hipGetLastError(); release(h); return MK_E_NOMEM; }
+  HIP_OR(hipMemset(h->ws, 0, h->wl.bytes));
+
+  // status mirror in pinned host memory mapped into the device
+  HIP_OR(hipHostMalloc(reinterpret_cast<void**>(&h->status_host), sizeof(mk::DevStatus), hipHostMallocMapped));
+  std::memset(h->status_host, 0, sizeof(mk::DevStatus));
+  HIP_OR(hipHostGetDevicePointer(reinterpret_cast<void**>(&h->status_host_dev), h->status_host, 0));
+
+  HIP_OR(hipStreamCreateWithFlags(&h->capture_stream, hipStreamNonBlocking));
+  int wclk_khz = 0;
+  HIP_OR(hipDeviceGetAttribute(&wclk_khz, hipDeviceAttributeWallClockRate, h->device));
+  const uint64_t ms = cfg->watchdog_ms > 0 ? (uint64_t)cfg->watchdog_ms : 2000ull;
+  h->watchdog_ticks = (uint64_t)(wclk_khz > 0 ? wclk_khz : 100000) * ms;
+  HIP_OR(hipDeviceSynchronize());
+  *out = h;
+  return MK_OK;
+}
+
+int mk_decode_step(mk_handle* h, const int32_t* d_token, int32_t pos, const mk_kv* kv, float* out_logits,
+                   int32_t* out_token, hipStream_t stream) {
+  if (!h || !d_token || !kv || !out_logits || !out_token) return MK_E_INVAL;
+  if (h->plan.L > 0 && (!kv->k || !kv->v)) return MK_E_INVAL;  // a 0-layer model has no cache
+  if ((reinterpret_cast<uintptr_t>(kv->k) | reinterpret_cast<uintptr_t>(kv->v)) & 3u) return MK_E_INVAL;
+  if ((reinterpret_cast<uintptr_t>(out_logits) | reinterpret_cast<uintptr_t>(out_token) |
+       reinterpret_cast<uintptr_t>(d_token)) & 3u)
+    return MK_E_INVAL;
+  if (pos < 0 || pos >= h->plan.S) return MK_E_RANGE;
+  if (reinterpret_cast<volatile int32_t*>(&h->status_host->code)[0] != MK_OK) return MK_E_STATE;
+  if (h->epoch + 1 >= kEpochLimit) {
+    if (clear_workspace(h, stream) != MK_OK) return MK_E_HIP;
+    h->epoch = 0;
+    h->shadow_pos = -1;
+  }
+  const uint32_t epoch = ++h->epoch;
+  Params P = make_params(h);
+  P.token = d_token;
+  P.kcache = kv->k;
+  P.vcache = kv->v;
+  P.logits = out_logits;
+  P.out_token = out_token;
+  P.pos = pos;
+  P.epoch = epoch;
+  hipError_t e = hipSuccess;
+  switch (h->cfg.exec_mode) {
+    case MK_MODE_MEGA:
+      e = mk::launch_persistent(P, h->plan.lds_bytes, stream);
+      break;
+    case MK_MODE_MULTI:
+      for (int s = 0; s < h->plan.stages && e == hipSuccess; ++s) e = mk::launch_stage(P, s, h->plan.lds_bytes, stream);
+      break;
+    case MK_MODE_GRAPH: {
+      const void* ptrs[5] = {d_token, kv->k, kv->v, out_logits, out_token};
+      if (!h->gexec || std::memcmp(ptrs, h->g_ptrs, sizeof(ptrs)) != 0) {
+        if (capture_graph(h, P) != MK_OK) return MK_E_HIP;
+        std::memcpy(h->g_ptrs, ptrs, sizeof(ptrs));
+      }
+      auto* dargs = reinterpret_cast<mk::StepArgs*>(h->ws + h->wl.dargs);
+      if (h->shadow_pos != pos || h->shadow_epoch != epoch) e = mk::launch_set_args(dargs, pos, epoch, stream);
+      if (e == hipSuccess) e = hipGraphLaunch(h->gexec, stream);
+      h->shadow_pos = pos + 1;
+      h->shadow_epoch = epoch + 1;
+      break;
+    }
+    default:
+      return MK_E_INVAL;
+  }
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return MK_E_HIP;
+  }
+  h->last_stream = stream;
+  h->used = true;
+  return MK_OK;
+}
+
+int mk_reset(mk_handle* h) {
+  if (!h) return MK_E_INVAL;
+  if (hipDeviceSynchronize() != hipSuccess) {
+    (void)hipGetLastError();
+    return MK_E_HIP;
+  }
+  if (hipMemset(h->ws, 0, h->wl.bytes) != hipSuccess) return MK_E_HIP;
+  if (hipDeviceSynchronize() != hipSuccess) return MK_E_HIP;
+  std::memset(h->status_host, 0, sizeof(mk::DevStatus));
+  h->epoch = 0;
+  h->shadow_pos = -1;
+  return MK_OK;
+}
+
+void mk_free(mk_handle* h) {
+  if (!h) return;
+  (void)hipDeviceSynchronize();
+  release(h);
+}
+
+int mk_status(mk_handle* h, mk_status_t* out) {
+  if (!h || !out) return MK_E_INVAL;
+  volatile mk::DevStatus* s = h->status_host;
+  out->code = s->code;
+  out->stage = s->stage;
+  out->wg = s->wg;
+  out->detail = s->detail;
+  return MK_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,137 @@
+// mk_internal.h -- structures shared by the host planner and the gfx950 kernels.
+//
+// The task tape is the "instruction sequences planned on the host once and
+// reused for every forward pass" of the article "Revolution der
+// KI-Beschleunigung: Wie ein Low-Latency Megakernel den Llama-1B Turbo
+// zuendet" (dasgeld.co): a [stage][workgroup] table of fixed-size task records.
+#ifndef MK_INTERNAL_H_
+#define MK_INTERNAL_H_
+
+#include <stdint.h>
+
+namespace mk {
+
+// Workgroup shape: 8 wave64s, one persistent workgroup per compute unit.
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+// A weight "unit" is 1 KiB: one 16-byte load per lane of a wave64.
+constexpr int kUnitBytes = 1024;
+constexpr int kUnitElems = kUnitBytes / 2;  // bf16 elements per unit
+// Rows are padded to a multiple of one unit.
+constexpr int kRowAlign = kUnitElems;
+// Per-wave LDS ring of weight units kept in flight (12 KiB per wave).
+constexpr int kRing = 12;
+// Largest group of query heads sharing one KV head.
+constexpr int kMaxGroup = 8;
+
+// Stage kinds, in their order within a layer; the LM head closes the tape.
+enum Op : uint8_t {
+  OP_NONE = 0,
+  OP_QKV = 1,    // attn RMSNorm + [Wq;Wk;Wv] GEMV + RoPE + KV append
+  OP_ATTN = 2,   // split-KV GQA decode attention (+ merge by the last chunk)
+  OP_OPROJ = 3,  // Wo GEMV + residual
+  OP_GU = 4,     // ffn RMSNorm + interleaved [gate;up] GEMV + SiLU*mul
+  OP_DOWN = 5,   // Wd GEMV + residual
+  OP_LM = 6,     // final RMSNorm + LM-head GEMV + argmax stage 1 (+ stage 2 by the last task)
+};
+
+inline constexpr bool op_is_gemv(int op) { return op == OP_QKV || op == OP_OPROJ || op == OP_GU || op == OP_DOWN || op == OP_LM; }
+
+constexpr int kStagesPerLayer = 5;
+
+// One tape entry (32 bytes, read with scalar loads).
+//  GEMV ops: row pairs [a0, a1) of the op's packed matrix; pair p occupies
+//            nu units starting at byte wofs + p * nu * kUnitBytes of the
+//            weight region selected by `region` (0 = arena, 1 = LM head).
+//  OP_ATTN : a0 = kv head, a1 = chunk index.
+struct Task {
+  uint8_t op;
+  uint8_t region;
+  uint16_t layer;
+  uint32_t a0;
+  uint32_t a1;
+  uint32_t nu;
+  uint64_t wofs;
+  uint32_t ntasks;  // tasks in this stage (argmax / merge participants)
+  uint32_t pad;
+};
+static_assert(sizeof(Task) == 32, "task record must stay 32 bytes");
+
+// Step arguments read from device memory by graph-captured launches.
+struct StepArgs {
+  int32_t pos;
+  uint32_t epoch;
+};
+
+// Device status (first error wins).  Mirrored into host-mapped memory.
+struct DevStatus {
+  int32_t code;
+  int32_t stage;
+  int32_t wg;
+  uint32_t detail;
+};
+
+// Kernel parameters (passed by value).
+struct Params {
+  const Task* tape;      // [num_stages][num_wgs]
+  int32_t num_wgs;
+  int32_t num_stages;
+
+  // model
+  int32_t L, H, Hp, QD, QDp, KVD, F, Fp, V, NQ, NKV, D, G, S, B;
+  float eps;
+  float qscale;          // 1 / sqrt(head_dim)
+  int32_t attn_chunks;
+
+  // weights
+  const char* arena;     // packed bf16 matrices (byte base)
+  const char* lm;        // LM-head matrix [V][Hp] (byte base)
+  const uint16_t* embed; // caller's [V][H] embedding
+  const float* g_attn;   // [L][Hp]
+  const float* g_ffn;    // [L][Hp]
+  const float* g_final;  // [Hp]
+  const float* rope;     // [S][D/2][2] cos, sin
+
+  // tagged activations: {fp32 value, epoch tag} per element
+  uint64_t* x_attn;      // [B][L][H]   residual after attention
+  uint64_t* x_ffn;       // [B][L][H]   residual after FFN
+  uint64_t* q;           // [B][L][QD]  rotated queries
+  uint64_t* kvcur;       // [B][L][2][KVD] this step's bf16-rounded k, v
+  uint64_t* o;           // [B][L][QD]  attention output
+  uint64_t* h;           // [B][L][F]   SwiGLU hidden
+  float* attn_part;      // [B][L][NKV][C][G*(D+2)] split-KV partials
+  uint32_t* attn_ctr;    // [B][L][NKV] merge counters (epoch * C per step)
+  uint64_t* amax;        // [B][num_wgs] argmax keys
+  uint32_t* amax_ctr;    // [B] argmax counters (epoch * tasks per step)
+  uint32_t* tokerr;      // [B] epoch of the last bad input token
+  uint32_t* abort_flag;  // non-zero: every workgroup stops
+  DevStatus* status;     // device copy of the status
+  DevStatus* status_host;// host-mapped mirror
+
+  // LDS layout (bytes from the dynamic LDS base)
+  int32_t lds_act;       // fp32 activation vector / attention scratch
+  int32_t lds_res;       // residual rows of the task
+  int32_t lds_rope;      // cos/sin of this position
+  int32_t lds_misc;      // reductions and flags
+  int32_t act_floats;
+  int32_t res_floats;
+
+  uint64_t watchdog_ticks;  // wall-clock ticks (100 MHz on MI355X)
+
+  // per step
+  const int32_t* token;  // [B]
+  uint16_t* kcache;      // [B][L][NKV][S][D]
+  uint16_t* vcache;
+  float* logits;         // [B][V]
+  int32_t* out_token;    // [B]
+  int32_t pos;
+  uint32_t epoch;
+  const StepArgs* dargs; // non-null: read pos and epoch from here (graph mode)
+};
+
+// LDS bytes of the per-wave rings.
+constexpr int kRingBytes = kWaves * kRing * kUnitBytes;
+
+}  // namespace mk
+
+#endif  // MK_INTERNAL_H_

@@ -1,0 +1,220 @@
+// mk_plan.cpp -- the host planner.
+//
+// The article "Revolution der KI-Beschleunigung: Wie ein Low-Latency
+// Megakernel den Llama-1B Turbo zuendet" (dasgeld.co) describes a GPU
+// interpreter that receives the forward pass as instruction sequences planned
+// on the host and reused, unchanged, for every forward pass.  Here the plan is
+// a [stage][workgroup] tape: every matrix op of every layer is cut into
+// contiguous row-pair ranges, one per workgroup, so each workgroup streams a
+// disjoint slice of every weight matrix exactly once per token.
+#include "mk_plan.h"
+
+#include <algorithm>
+#include <cstring>
+
+namespace mk {
+
+namespace {
+
+inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
+inline uint64_t round_up64(uint64_t x, uint64_t m) { return (x + m - 1) / m * m; }
+
+int fail(Plan& p, int code, const char* msg) {
+  p.error = msg;
+  return code;
+}
+
+}  // namespace
+
+uint64_t qkv_rows(const Plan& p) { return (uint64_t)p.QD + 2ull * p.KVD; }
+
+int plan_build(const mk_config& c, int W, Plan& p) {
+  p = Plan();
+  if (c.n_layers < 0 || c.hidden <= 0 || c.n_heads <= 0 || c.n_kv_heads <= 0 || c.head_dim <= 0 || c.ffn <= 0 ||
+      c.vocab <= 0 || c.max_seq <= 0 || c.batch <= 0)
+    return fail(p, MK_E_INVAL, "dimensions must be positive (n_layers >= 0)");
+  if (c.n_heads % c.n_kv_heads != 0) return fail(p, MK_E_INVAL, "n_heads must be a multiple of n_kv_heads");
+  if (c.head_dim % 8 != 0 || kThreads % c.head_dim != 0)
+    return fail(p, MK_E_UNSUPPORTED, "head_dim must be a multiple of 8 dividing 512");
+  if (c.hidden % 2 != 0 || c.vocab % 2 != 0) return fail(p, MK_E_UNSUPPORTED, "hidden and vocab must be even");
+  if (c.n_heads / c.n_kv_heads > kMaxGroup) return fail(p, MK_E_UNSUPPORTED, "more than 8 query heads per kv head");
+  if (c.batch != 1) return fail(p, MK_E_UNSUPPORTED, "this build decodes batch 1");
+  if (!(c.rms_eps >= 0.0f) || !(c.rope_theta > 0.0)) return fail(p, MK_E_INVAL, "rms_eps >= 0 and rope_theta > 0");
+  if (c.exec_mode < MK_MODE_MEGA || c.exec_mode > MK_MODE_GRAPH) return fail(p, MK_E_INVAL, "unknown exec_mode");
+  if (W <= 0 || W > 4096) return fail(p, MK_E_INVAL, "workgroup count out of range");
+
+  p.L = c.n_layers;
+  p.H = c.hidden;
+  p.NQ = c.n_heads;
+  p.NKV = c.n_kv_heads;
+  p.D = c.head_dim;
+  p.G = c.n_heads / c.n_kv_heads;
+  p.QD = c.n_heads * c.head_dim;
+  p.KVD = c.n_kv_heads * c.head_dim;
+  p.F = c.ffn;
+  p.V = c.vocab;
+  p.S = c.max_seq;
+  p.B = c.batch;
+  p.W = W;
+  p.tied = c.tie_embeddings != 0;
+  p.Hp = round_up(p.H, kRowAlign);
+  p.QDp = round_up(p.QD, kRowAlign);
+  p.Fp = round_up(p.F, kRowAlign);
+
+  // Attention split: chunks of at most 256 positions, at most one task per workgroup.
+  int C = c.attn_chunks;
+  if (C <= 0) C = (p.S + 255) / 256;
+  C = std::max(1, std::min(C, p.S));
+  if ((int64_t)C * p.NKV > W) C = std::max(1, W / p.NKV);
+  if ((int64_t)C * p.NKV > W) return fail(p, MK_E_UNSUPPORTED, "more kv heads than workgroups");
+  p.C = C;
+  const int lmax = (p.S + C - 1) / C;  // longest chunk
+
+  // ---- packed arena layout: per layer [Wq;Wk;Wv] | Wo | [gate/up interleaved] | Wd
+  const uint64_t align = 4096;
+  uint64_t off = 0;
+  p.off_qkv.resize(p.L);
+  p.off_o.resize(p.L);
+  p.off_gu.resize(p.L);
+  p.off_down.resize(p.L);
+  for (int l = 0; l < p.L; ++l) {
+    p.off_qkv[l] = off;
+    off = round_up64(off + qkv_rows(p) * p.Hp * 2, align);
+    p.off_o[l] = off;
+    off = round_up64(off + (uint64_t)p.H * p.QDp * 2, align);
+    p.off_gu[l] = off;
+    off = round_up64(off + 2ull * p.F * p.Hp * 2, align);
+    p.off_down[l] = off;
+    off = round_up64(off + (uint64_t)p.H * p.Fp * 2, align);
+  }
+  p.arena_bytes = std::max<uint64_t>(off, align);
+  p.lm_borrowed = (p.Hp == p.H);
+  p.lm_bytes = p.lm_borrowed ? 0 : (uint64_t)p.V * p.Hp * 2;
+
+  // ---- tape
+  p.stages = kStagesPerLayer * p.L + 1;
+  p.tape.assign((size_t)p.stages * W, Task{});
+  int max_res_rows = 0;
+  auto gemv_stage = [&](int s, Op op, int layer, uint64_t pairs, uint32_t nu, uint64_t wofs, uint8_t region) {
+    uint32_t n = 0;
+    for (int b = 0; b < W; ++b) {
+      uint64_t a0 = pairs * (uint64_t)b / W, a1 = pairs * (uint64_t)(b + 1) / W;
+      if (a1 > a0) ++n;
+    }
+    for (int b = 0; b < W; ++b) {
+      uint64_t a0 = pairs * (uint64_t)b / W, a1 = pairs * (uint64_t)(b + 1) / W;
+      Task& t = p.tape[(size_t)s * W + b];
+      if (a1 == a0) continue;
+      t.op = op;
+      t.region = region;
+      t.layer = (uint16_t)layer;
+      t.a0 = (uint32_t)a0;
+      t.a1 = (uint32_t)a1;
+      t.nu = nu;
+      t.wofs = wofs;
+      t.ntasks = n;
+      if (op == OP_OPROJ || op == OP_DOWN) max_res_rows = std::max(max_res_rows, (int)(2 * (a1 - a0)));
+    }
+  };
+  for (int l = 0; l < p.L; ++l) {
+    const int s0 = kStagesPerLayer * l;
+    gemv_stage(s0 + 0, OP_QKV, l, qkv_rows(p) / 2, (uint32_t)(2 * p.Hp / kUnitElems), p.off_qkv[l], 0);
+    // attention: task i = (kv head i / C, chunk i % C) on workgroup i
+    for (int i = 0; i < p.NKV * C; ++i) {
+      Task& t = p.tape[(size_t)(s0 + 1) * W + i];
+      t.op = OP_ATTN;
+      t.layer = (uint16_t)l;
+      t.a0 = (uint32_t)(i / C);
+      t.a1 = (uint32_t)(i % C);
+      t.ntasks = (uint32_t)(p.NKV * C);
+    }
+    gemv_stage(s0 + 2, OP_OPROJ, l, p.H / 2, (uint32_t)(2 * p.QDp / kUnitElems), p.off_o[l], 0);
+    gemv_stage(s0 + 3, OP_GU, l, p.F, (uint32_t)(2 * p.Hp / kUnitElems), p.off_gu[l], 0);
+    gemv_stage(s0 + 4, OP_DOWN, l, p.H / 2, (uint32_t)(2 * p.Fp / kUnitElems), p.off_down[l], 0);
+  }
+  gemv_stage(p.stages - 1, OP_LM, p.L, p.V / 2, (uint32_t)(2 * p.Hp / kUnitElems), 0, 1);
+  p.num_tasks = 0;
+  for (const Task& t : p.tape) p.num_tasks += t.op != OP_NONE;
+
+  // ---- LDS layout
+  const int np = kThreads / p.D;  // position partitions in the attention PV loop
+  const int attn_floats = p.G * p.D + 2 * p.D + lmax * p.G + np * p.G * p.D + 4 * kMaxGroup;
+  p.act_floats = round_up(std::max(std::max(p.Hp, p.QDp), std::max(p.Fp, attn_floats)), 4);
+  p.res_floats = round_up(std::max(max_res_rows, 4), 4);
+  p.lds_act = kRingBytes;
+  p.lds_res = p.lds_act + p.act_floats * 4;
+  p.lds_rope = p.lds_res + p.res_floats * 4;
+  p.lds_misc = p.lds_rope + round_up(p.D, 4) * 4;
+  p.lds_bytes = p.lds_misc + 256;
+  if (p.lds_bytes > 160 * 1024) return fail(p, MK_E_UNSUPPORTED, "LDS plan exceeds 160 KiB per workgroup");
+  return MK_OK;
+}
+
+int plan_validate(const Plan& p, std::string* why) {
+  auto bad = [&](const std::string& m) {
+    if (why) *why = m;
+    return MK_E_INVAL;
+  };
+  const int W = p.W;
+  if ((int)p.tape.size() != p.stages * W) return bad("tape size");
+  for (int s = 0; s < p.stages; ++s) {
+    const bool lm = s == p.stages - 1;
+    const int kind = lm ? OP_LM : 1 + (s % kStagesPerLayer);
+    const int layer = lm ? p.L : s / kStagesPerLayer;
+    uint64_t pairs = 0, nu = 0, wofs = 0, region_bytes = 0;
+    switch (kind) {
+      case OP_QKV:
+        pairs = qkv_rows(p) / 2; nu = 2 * p.Hp / kUnitElems; wofs = p.off_qkv[layer];
+        region_bytes = qkv_rows(p) * p.Hp * 2; break;
+      case OP_OPROJ:
+        pairs = p.H / 2; nu = 2 * p.QDp / kUnitElems; wofs = p.off_o[layer];
+        region_bytes = (uint64_t)p.H * p.QDp * 2; break;
+      case OP_GU:
+        pairs = p.F; nu = 2 * p.Hp / kUnitElems; wofs = p.off_gu[layer];
+        region_bytes = 2ull * p.F * p.Hp * 2; break;
+      case OP_DOWN:
+        pairs = p.H / 2; nu = 2 * p.Fp / kUnitElems; wofs = p.off_down[layer];
+        region_bytes = (uint64_t)p.H * p.Fp * 2; break;
+      case OP_LM:
+        pairs = p.V / 2; nu = 2 * p.Hp / kUnitElems; wofs = 0;
+        region_bytes = (uint64_t)p.V * p.Hp * 2; break;
+      default: break;
+    }
+    uint32_t count = 0;
+    for (int b = 0; b < W; ++b) count += p.tape[(size_t)s * W + b].op != OP_NONE;
+    if (kind == OP_ATTN) {
+      std::vector<int> seen((size_t)p.NKV * p.C, 0);
+      for (int b = 0; b < W; ++b) {
+        const Task& t = p.tape[(size_t)s * W + b];
+        if (t.op == OP_NONE) continue;
+        if (t.op != OP_ATTN || t.layer != layer) return bad("attention stage holds another op");
+        if ((int)t.a0 >= p.NKV || (int)t.a1 >= p.C) return bad("attention task out of range");
+        if (seen[(size_t)t.a0 * p.C + t.a1]++) return bad("attention task repeated");
+        if (t.ntasks != count) return bad("attention task count");
+      }
+      for (int v : seen)
+        if (v != 1) return bad("attention task missing");
+      continue;
+    }
+    // GEMV: ranges must tile [0, pairs) exactly, in workgroup order
+    uint64_t next = 0;
+    for (int b = 0; b < W; ++b) {
+      const Task& t = p.tape[(size_t)s * W + b];
+      if (t.op == OP_NONE) continue;
+      if (t.op != kind || t.layer != layer) return bad("stage holds another op");
+      if (t.a0 != next || t.a1 <= t.a0) return bad("row pairs not tiled exactly");
+      next = t.a1;
+      if (t.nu != nu || t.wofs != wofs) return bad("task geometry");
+      if ((uint64_t)t.a1 * t.nu * kUnitBytes > region_bytes) return bad("task reads past its matrix");
+      if (t.ntasks != count) return bad("task count");
+      if ((kind == OP_OPROJ || kind == OP_DOWN) && 2 * (t.a1 - t.a0) > (uint32_t)p.res_floats)
+        return bad("residual rows exceed LDS");
+      if (t.region != (kind == OP_LM ? 1 : 0)) return bad("weight region");
+    }
+    if (next != pairs) return bad("row pairs not covered");
+  }
+  if (p.lds_bytes > 160 * 1024) return bad("LDS");
+  return MK_OK;
+}
+
+}  // namespace mk

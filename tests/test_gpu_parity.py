@@ -1,0 +1,149 @@
+"""GPU parity of the megakernel (and the launch-per-stage baselines) against
+the CPU oracle, through the C ABI.  Run on an MI355X: pytest -m gpu."""
+
+import numpy as np
+import pytest
+
+import oracle as orc
+from synth_inputs import LLAMA_1B, TINY, make_kv_cache, make_prompt, make_start_token, make_weights
+from tests.parity import GpuDecoder, log, logit_tol, run_teacher_forced
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tiny_w():
+    return make_weights(TINY, master=0, gain_jitter=0.1)
+
+
+@pytest.mark.parametrize("mode", ["mega", "multi", "graph"])
+def test_tiny_prompt_and_greedy(tiny_w, mode):
+    # tiny decoder: 16-token prompt, then 32 greedy steps (positions 0..47)
+    prompt = make_prompt(TINY, 16)
+    run_teacher_forced(TINY, tiny_w, 48, prompt, 0, 32, mode=mode, label="tiny")
+
+
+def test_tiny_unit_gains_untied():
+    sh = TINY.with_(tie_embeddings=False)
+    w = make_weights(sh, master=3)
+    run_teacher_forced(sh, w, 48, make_prompt(sh, 8, master=3), 0, 8, mode="mega", label="tiny-untied")
+
+
+def test_tiny_chunked_attention(tiny_w):
+    # split-KV partials merged by the last chunk of each kv head
+    run_teacher_forced(TINY, tiny_w, 48, make_prompt(TINY, 12), 0, 8, mode="mega", attn_chunks=4,
+                       label="tiny-chunks4")
+
+
+def test_tiny_zero_layers_identity():
+    sh = TINY.with_(n_layers=0)
+    w = make_weights(sh, master=0)
+    gpu = GpuDecoder(sh, w, 8, mode="mega")
+    try:
+        rng = np.random.default_rng(5)
+        for tok in rng.integers(0, sh.vocab, 64):
+            lg, out = gpu.step(int(tok), 0)
+            assert out == int(tok)
+    finally:
+        gpu.close()
+
+
+@pytest.fixture(scope="module")
+def llama1b():
+    w = make_weights(LLAMA_1B, master=0)
+    return w, orc.Oracle(LLAMA_1B, w)
+
+
+@pytest.mark.parametrize("mode", ["mega", "graph"])
+def test_llama1b_shape_short(llama1b, mode):
+    # Llama-1B shape: a 4-token prompt and 4 greedy steps (oracle cost bounds the length)
+    w, o = llama1b
+    run_teacher_forced(LLAMA_1B, w, 256, make_prompt(LLAMA_1B, 4), 0, 4, mode=mode, oracle_obj=o,
+                       label="llama1b")
+
+
+def test_llama1b_repeat_bit_identical(llama1b):
+    # the same steps from the same cache give bit-identical logits and tokens, every time
+    w, _ = llama1b
+    gpu = GpuDecoder(LLAMA_1B, w, 256, mode="mega")
+    toks = [int(t) for t in make_prompt(LLAMA_1B, 6, master=7)]
+    try:
+        first = None
+        for rep in range(6):
+            gpu.k.zero_()
+            gpu.v.zero_()
+            run = [gpu.step(t, p) for p, t in enumerate(toks)]
+            if first is None:
+                first = run
+            for (a, ta), (b, tb) in zip(first, run):
+                assert ta == tb and np.array_equal(a, b), f"repeat {rep} differs"
+    finally:
+        gpu.close()
+
+
+def test_llama1b_long_context_positions(llama1b):
+    # seeded N(0,1) cache of 8192 slots; single steps at 4096 and 8191 with 32 attention chunks
+    sh = LLAMA_1B
+    w, o = llama1b
+    kv = make_kv_cache(sh, 1, 8192, 8192, master=0)
+    tok = make_start_token(sh, 0)
+    gpu = GpuDecoder(sh, w, 8192, mode="mega", kv_init=kv)
+    kc, vc = kv[0][0].copy(), kv[1][0].copy()   # both sides carry the slot written at 4096 into 8191
+    try:
+        for pos in (4096, 8191):
+            lg_ref = o.decode_step(tok, pos, kc, vc)
+            lg, out = gpu.step(tok, pos)
+            err = float(np.max(np.abs(lg - lg_ref)))
+            log(f"[parity] long pos={pos} err/tol={err / logit_tol(lg_ref):.3g}")
+            assert err <= logit_tol(lg_ref)
+            assert out == int(np.argmax(lg))
+    finally:
+        gpu.close()
+
+
+def test_determinism_and_nan_poison(tiny_w):
+    # the same step twice is bit-identical; slots above pos are never read
+    gpu = GpuDecoder(TINY, tiny_w, 48, mode="mega")
+    try:
+        for p, t in enumerate(make_prompt(TINY, 10)):
+            gpu.step(int(t), p)
+        k0, v0 = gpu.k.clone(), gpu.v.clone()
+        a, ta = gpu.step(77, 10)
+        gpu.k.copy_(k0)
+        gpu.v.copy_(v0)
+        b, tb = gpu.step(77, 10)
+        assert np.array_equal(a, b) and ta == tb
+        gpu.k.copy_(k0)
+        gpu.v.copy_(v0)
+        gpu.k[:, :, :, 11:, :] = 0x7FC0   # bf16 NaN
+        gpu.v[:, :, :, 11:, :] = 0x7FC0
+        c, tc = gpu.step(77, 10)
+        assert np.array_equal(a, c) and ta == tc
+    finally:
+        gpu.close()
+
+
+def test_error_paths(tiny_w):
+    from persistent_megakernel_cu_amd import binding as mkb
+    gpu = GpuDecoder(TINY, tiny_w, 48, mode="mega")
+    try:
+        with pytest.raises(mkb.MkError) as e:
+            gpu.eng.decode_step(gpu.tok, 48, gpu.k, gpu.v, gpu.logits, gpu.out_tok)
+        assert e.value.code == mkb.MK_E_RANGE
+        with pytest.raises(mkb.MkError) as e:
+            gpu.eng.decode_step(gpu.tok, -1, gpu.k, gpu.v, gpu.logits, gpu.out_tok)
+        assert e.value.code == mkb.MK_E_RANGE
+        # a bad token id is caught on the device: out_token = -1 and MK_E_TOKEN latched
+        lg, out = gpu.step(TINY.vocab + 5, 0)
+        assert out == -1
+        st = gpu.eng.status()
+        assert st.code == mkb.MK_E_TOKEN and st.detail == TINY.vocab + 5
+        with pytest.raises(mkb.MkError) as e:
+            gpu.step(1, 1)
+        assert e.value.code == mkb.MK_E_STATE
+        gpu.eng.reset()
+        assert gpu.eng.status().code == 0
+        lg, out = gpu.step(1, 0)
+        assert out == int(np.argmax(lg))
+    finally:
+        gpu.close()

@@ -1,0 +1,81 @@
+"""Host-only checks of libmk.so: it loads without a GPU, exports every function
+include/mk.h declares, and its planner builds and validates the task tape."""
+
+import ctypes
+
+import pytest
+
+from persistent_megakernel_cu_amd import binding as mkb
+from synth_inputs import LLAMA_1B, LLAMA_8B, TINY
+
+
+def test_exports_every_declared_function():
+    names = mkb.header_functions()
+    assert set(names) == {"mk_load", "mk_decode_step", "mk_reset", "mk_free", "mk_status", "mk_error_string",
+                          "mk_plan_describe"}
+    L = mkb.lib()
+    for n in names:
+        assert getattr(L, n) is not None
+
+
+def test_error_strings():
+    for code in range(0, -10, -1):
+        assert mkb.error_string(code) and mkb.error_string(code) != "unknown error"
+    assert mkb.error_string(-99) == "unknown error"
+
+
+@pytest.mark.parametrize("shape,max_seq,chunks", [
+    (TINY, 48, 1), (LLAMA_1B, 256, 1), (LLAMA_1B, 8192, 32), (LLAMA_1B, 1088, 5), (LLAMA_8B, 2112, 9)])
+def test_plan_validates(shape, max_seq, chunks):
+    info = mkb.plan_describe(shape, max_seq, 256)
+    assert info.num_stages == 5 * shape.n_layers + 1
+    assert info.attn_chunks == chunks
+    assert info.lds_bytes <= 160 * 1024
+    # every byte of every matrix is in the packed arena once (LM head borrowed when rows need no padding)
+    H, QD, KVD, F = shape.hidden, shape.q_dim, shape.kv_dim, shape.ffn
+    per_layer = 2 * (QD * H + 2 * KVD * H + H * QD + 2 * F * H + H * F)
+    if H % 512 == 0 and QD % 512 == 0 and F % 512 == 0:
+        assert info.weight_bytes >= shape.n_layers * per_layer
+        assert info.weight_bytes <= shape.n_layers * per_layer + 5 * shape.n_layers * 4096
+
+
+@pytest.mark.parametrize("wgs", [2, 7, 64, 255, 256])
+def test_plan_any_workgroup_count(wgs):
+    info = mkb.plan_describe(TINY, 48, wgs)
+    assert info.num_wgs == wgs
+
+
+def test_plan_needs_a_workgroup_per_kv_head():
+    # one task per (stage, workgroup): attention needs at least n_kv_heads workgroups
+    with pytest.raises(mkb.MkError) as e:
+        mkb.plan_describe(TINY, 48, 1)
+    assert e.value.code == mkb.MK_E_UNSUPPORTED
+
+
+def test_plan_rejects_bad_configs():
+    bad = [
+        dict(n_heads=3),            # not a multiple of n_kv_heads
+        dict(head_dim=12),          # not a multiple of 8 dividing 512
+        dict(hidden=255),           # odd
+    ]
+    for kw in bad:
+        sh = TINY.with_(**kw)
+        with pytest.raises(mkb.MkError):
+            mkb.plan_describe(sh, 48, 256)
+    with pytest.raises(mkb.MkError) as e:
+        mkb.plan_describe(TINY, 48, 256, batch=2)
+    assert e.value.code == mkb.MK_E_UNSUPPORTED
+    c = mkb.make_config(TINY, 48)
+    info = mkb.MkPlanInfo()
+    assert mkb.lib().mk_plan_describe(None, 256, ctypes.byref(info)) == mkb.MK_E_INVAL
+    assert mkb.lib().mk_plan_describe(ctypes.byref(c), 256, None) == mkb.MK_E_INVAL
+
+
+def test_null_arguments_are_rejected():
+    L = mkb.lib()
+    h = ctypes.c_void_p()
+    assert L.mk_load(None, None, ctypes.byref(h)) == mkb.MK_E_INVAL
+    assert L.mk_decode_step(None, None, 0, None, None, None, None) == mkb.MK_E_INVAL
+    assert L.mk_reset(None) == mkb.MK_E_INVAL
+    assert L.mk_status(None, None) == mkb.MK_E_INVAL
+    L.mk_free(None)
