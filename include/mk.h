@@ -65,7 +65,9 @@ extern "C" {
  * embedding matrix as LM head.  exec_mode is one of MK_MODE_*.
  * attn_chunks: split of [0, pos] per KV head in attention (0 = automatic).
  * num_wgs: persistent workgroups (0 = one per compute unit).
- * watchdog_ms: budget of any single dependency wait (0 = 2000 ms). */
+ * watchdog_ms: budget of any single dependency wait (0 = 2000 ms).
+ * trace: non-zero records, for every (workgroup, stage) of the latest step,
+ * four device wall-clock stamps (see mk_trace_copy); off for timing runs. */
 typedef struct mk_config {
   int32_t n_layers;
   int32_t hidden;
@@ -83,7 +85,8 @@ typedef struct mk_config {
   int32_t attn_chunks;
   int32_t num_wgs;
   int32_t watchdog_ms;
-  int32_t reserved[7];
+  int32_t trace;
+  int32_t reserved[6];
 } mk_config;
 
 /* Device pointers to one layer's bf16 weights (row-major [out][in]):
@@ -187,6 +190,17 @@ int mk_status(mk_handle* h, mk_status_t* out);
 
 /* mk_error_string -- static text for an MK_* code. */
 const char* mk_error_string(int code);
+
+/* mk_trace_copy -- wait for the device, then copy the trace of the latest
+ * step into host memory out[capacity_words]: num_wgs * num_stages records of
+ * four uint64 stamps {stage entered, inputs ready, compute done, stage left}
+ * read from the device-wide constant-rate clock (s_memrealtime), record
+ * (wg, stage) at word 4 * (wg * num_stages + stage); a stamp of 0 means the
+ * workgroup had no task in that stage.  *words_written gets the word count and
+ * *clock_khz the clock rate.  Errors: MK_E_INVAL (null, capacity too small,
+ * handle loaded without cfg.trace), MK_E_HIP. */
+int mk_trace_copy(mk_handle* h, uint64_t* out, int64_t capacity_words, int64_t* words_written,
+                  int32_t* clock_khz);
 
 /* mk_plan_describe -- build and validate the task tape for cfg on num_wgs
  * workgroups (0 = assume 256) on the HOST ONLY, without touching a GPU, and

@@ -40,7 +40,7 @@ class MkConfig(ctypes.Structure):
         ("vocab", ctypes.c_int32), ("max_seq", ctypes.c_int32), ("batch", ctypes.c_int32),
         ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_double), ("tie_embeddings", ctypes.c_int32),
         ("exec_mode", ctypes.c_int32), ("attn_chunks", ctypes.c_int32), ("num_wgs", ctypes.c_int32),
-        ("watchdog_ms", ctypes.c_int32), ("reserved", ctypes.c_int32 * 7),
+        ("watchdog_ms", ctypes.c_int32), ("trace", ctypes.c_int32), ("reserved", ctypes.c_int32 * 6),
     ]
 
 
@@ -101,6 +101,9 @@ def lib() -> ctypes.CDLL:
         L.mk_error_string.restype = ctypes.c_char_p
         L.mk_plan_describe.argtypes = [ctypes.POINTER(MkConfig), ctypes.c_int32, ctypes.POINTER(MkPlanInfo)]
         L.mk_plan_describe.restype = ctypes.c_int
+        L.mk_trace_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64),
+                                    ctypes.POINTER(ctypes.c_int32)]
+        L.mk_trace_copy.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -116,7 +119,7 @@ def error_string(code: int) -> str:
 
 
 def make_config(shape, max_seq: int, batch: int = 1, mode: str | int = "mega", attn_chunks: int = 0,
-                num_wgs: int = 0, watchdog_ms: int = 0) -> MkConfig:
+                num_wgs: int = 0, watchdog_ms: int = 0, trace: bool = False) -> MkConfig:
     c = MkConfig()
     c.n_layers, c.hidden, c.n_heads = shape.n_layers, shape.hidden, shape.n_heads
     c.n_kv_heads, c.head_dim, c.ffn, c.vocab = shape.n_kv_heads, shape.head_dim, shape.ffn, shape.vocab
@@ -125,6 +128,7 @@ def make_config(shape, max_seq: int, batch: int = 1, mode: str | int = "mega", a
     c.tie_embeddings = 1 if shape.tie_embeddings else 0
     c.exec_mode = MODES[mode] if isinstance(mode, str) else int(mode)
     c.attn_chunks, c.num_wgs, c.watchdog_ms = attn_chunks, num_wgs, watchdog_ms
+    c.trace = 1 if trace else 0
     return c
 
 
@@ -146,11 +150,11 @@ class Engine:
     """
 
     def __init__(self, shape, weights: dict, max_seq: int, mode: str = "mega", batch: int = 1,
-                 attn_chunks: int = 0, num_wgs: int = 0, watchdog_ms: int = 0):
+                 attn_chunks: int = 0, num_wgs: int = 0, watchdog_ms: int = 0, trace: bool = False):
         self.shape = shape
         self.max_seq = max_seq
         self.batch = batch
-        self.cfg = make_config(shape, max_seq, batch, mode, attn_chunks, num_wgs, watchdog_ms)
+        self.cfg = make_config(shape, max_seq, batch, mode, attn_chunks, num_wgs, watchdog_ms, trace)
         ptr = lambda name: ctypes.c_void_p(weights[name].data_ptr())
         layers = (MkLayerWeights * max(1, shape.n_layers))()
         for l in range(shape.n_layers):
@@ -183,6 +187,22 @@ class Engine:
                                   out_token.data_ptr(), ctypes.c_void_p(stream))
         if rc != MK_OK:
             raise MkError(rc, "mk_decode_step")
+
+    def trace(self):
+        """Stamps of the latest step as (numpy uint64 [wg][stage][4], clock kHz)."""
+        import numpy as np
+        info = MkPlanInfo()
+        rc = lib().mk_plan_describe(ctypes.byref(self.cfg), self.cfg.num_wgs or 256, ctypes.byref(info))
+        if rc != MK_OK:
+            raise MkError(rc, "mk_plan_describe")
+        cap = 4 * 4096 * info.num_stages
+        buf = np.zeros(cap, dtype=np.uint64)
+        n = ctypes.c_int64()
+        khz = ctypes.c_int32()
+        rc = lib().mk_trace_copy(self._h, buf.ctypes.data, cap, ctypes.byref(n), ctypes.byref(khz))
+        if rc != MK_OK:
+            raise MkError(rc, "mk_trace_copy")
+        return buf[: n.value].reshape(-1, info.num_stages, 4), khz.value
 
     def status(self) -> MkStatus:
         s = MkStatus()

@@ -12,8 +12,8 @@
 #include "mk_plan.h"
 
 namespace mk {
-hipError_t configure_kernels(int lds_bytes);
-hipError_t persistent_occupancy(int lds_bytes, int* blocks_per_cu);
+hipError_t configure_kernels(int G, int D, int lds_bytes);
+hipError_t persistent_occupancy(int G, int D, int lds_bytes, int* blocks_per_cu);
 hipError_t launch_persistent(const Params& P, int lds_bytes, hipStream_t stream);
 hipError_t launch_stage(const Params& P, int s, int lds_bytes, hipStream_t stream);
 hipError_t launch_set_args(StepArgs* a, int pos, uint32_t epoch, hipStream_t stream);
@@ -75,6 +75,8 @@ struct mk_handle {
   float* rope = nullptr;
   mk::Task* tape = nullptr;
   char* ws = nullptr;
+  uint64_t* trace = nullptr;  // [W][stages][4] when cfg.trace
+  int clock_khz = 0;
   Workspace wl{};
   mk::DevStatus* status_host = nullptr;     // pinned, host-mapped
   mk::DevStatus* status_host_dev = nullptr; // its device address
@@ -104,6 +106,7 @@ void release(mk_handle* h) {
   if (h->rope) (void)hipFree(h->rope);
   if (h->tape) (void)hipFree(h->tape);
   if (h->ws) (void)hipFree(h->ws);
+  if (h->trace) (void)hipFree(h->trace);
   if (h->status_host) (void)hipHostFree(h->status_host);
   delete h;
 }
@@ -146,9 +149,11 @@ Params make_params(mk_handle* h) {
   P.lds_res = p.lds_res;
   P.lds_rope = p.lds_rope;
   P.lds_misc = p.lds_misc;
+  P.lds_part = p.lds_part;
   P.act_floats = p.act_floats;
   P.res_floats = p.res_floats;
   P.watchdog_ticks = h->watchdog_ticks;
+  P.trace = h->trace;
   return P;
 }
 
@@ -269,9 +274,9 @@ int mk_load(const mk_config* cfg, const mk_weights* w, mk_handle** out) {
   const Plan& p = h->plan;
 
   // persistent residency: one workgroup per compute unit must fit
-  HIP_OR(mk::configure_kernels(p.lds_bytes));
+  HIP_OR(mk::configure_kernels(p.G, p.D, p.lds_bytes));
   int per_cu = 0;
-  HIP_OR(mk::persistent_occupancy(p.lds_bytes, &per_cu));
+  HIP_OR(mk::persistent_occupancy(p.G, p.D, p.lds_bytes, &per_cu));
   if (per_cu < 1) { release(h); return MK_E_DEVICE; }
 
   // packed weights
@@ -346,8 +351,14 @@ int mk_load(const mk_config* cfg, const mk_weights* w, mk_handle** out) {
   HIP_OR(hipHostGetDevicePointer(reinterpret_cast<void**>(&h->status_host_dev), h->status_host, 0));
 
   HIP_OR(hipStreamCreateWithFlags(&h->capture_stream, hipStreamNonBlocking));
+  if (cfg->trace) {
+    const size_t tb = (size_t)p.W * p.stages * 4 * sizeof(uint64_t);
+    HIP_OR(hipMalloc(&h->trace, tb));
+    HIP_OR(hipMemset(h->trace, 0, tb));
+  }
   int wclk_khz = 0;
   HIP_OR(hipDeviceGetAttribute(&wclk_khz, hipDeviceAttributeWallClockRate, h->device));
+  h->clock_khz = wclk_khz > 0 ? wclk_khz : 100000;
   const uint64_t ms = cfg->watchdog_ms > 0 ? (uint64_t)cfg->watchdog_ms : 2000ull;
   h->watchdog_ticks = (uint64_t)(wclk_khz > 0 ? wclk_khz : 100000) * ms;
   HIP_OR(hipDeviceSynchronize());
@@ -430,6 +441,20 @@ void mk_free(mk_handle* h) {
   if (!h) return;
   (void)hipDeviceSynchronize();
   release(h);
+}
+
+int mk_trace_copy(mk_handle* h, uint64_t* out, int64_t capacity_words, int64_t* words_written, int32_t* clock_khz) {
+  if (!h || !out || !h->trace) return MK_E_INVAL;
+  const int64_t n = (int64_t)h->plan.W * h->plan.stages * 4;
+  if (capacity_words < n) return MK_E_INVAL;
+  if (hipDeviceSynchronize() != hipSuccess) {
+    (void)hipGetLastError();
+    return MK_E_HIP;
+  }
+  if (hipMemcpy(out, h->trace, (size_t)n * sizeof(uint64_t), hipMemcpyDeviceToHost) != hipSuccess) return MK_E_HIP;
+  if (words_written) *words_written = n;
+  if (clock_khz) *clock_khz = h->clock_khz;
+  return MK_OK;
 }
 
 int mk_status(mk_handle* h, mk_status_t* out) {

@@ -23,6 +23,10 @@ constexpr int kRowAlign = kUnitElems;
 constexpr int kRing = 12;
 // Largest group of query heads sharing one KV head.
 constexpr int kMaxGroup = 8;
+// Largest number of split items (pairs << kslog) of one task (LDS partials).
+constexpr int kMaxItems = 256;
+// Longest attention chunk (positions) one task handles.
+constexpr int kMaxChunk = 256;
 
 // Stage kinds, in their order within a layer; the LM head closes the tape.
 enum Op : uint8_t {
@@ -43,6 +47,10 @@ constexpr int kStagesPerLayer = 5;
 //  GEMV ops: row pairs [a0, a1) of the op's packed matrix; pair p occupies
 //            nu units starting at byte wofs + p * nu * kUnitBytes of the
 //            weight region selected by `region` (0 = arena, 1 = LM head).
+//            Each pair is cut into 2^kslog work items: with kslog == 0 an item
+//            is the whole pair and one wave finishes it; otherwise an item is
+//            a run of nu >> kslog units inside one row, and the partial sums
+//            of a pair's items are added in LDS in item order.
 //  OP_ATTN : a0 = kv head, a1 = chunk index.
 struct Task {
   uint8_t op;
@@ -53,7 +61,7 @@ struct Task {
   uint32_t nu;
   uint64_t wofs;
   uint32_t ntasks;  // tasks in this stage (argmax / merge participants)
-  uint32_t pad;
+  uint32_t kslog;
 };
 static_assert(sizeof(Task) == 32, "task record must stay 32 bytes");
 
@@ -113,10 +121,12 @@ struct Params {
   int32_t lds_res;       // residual rows of the task
   int32_t lds_rope;      // cos/sin of this position
   int32_t lds_misc;      // reductions and flags
+  int32_t lds_part;      // [kMaxItems] partial sums of split items
   int32_t act_floats;
   int32_t res_floats;
 
   uint64_t watchdog_ticks;  // wall-clock ticks (100 MHz on MI355X)
+  uint64_t* trace;          // [num_wgs][num_stages][4] stamps, or null
 
   // per step
   const int32_t* token;  // [B]

@@ -96,15 +96,32 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
+// Cross-lane data movement within rows of 16 lanes (DPP).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Wave64 sum: butterflies inside each 16-lane row (quad_perm xor 1, xor 2,
+// row_half_mirror, row_mirror) leave every lane of a row with the row total,
+// then the four row totals are added in a fixed order.  Every lane returns the
+// same value.  Must be called with all 64 lanes active.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x141>(v);
+  v += dpp<0x140>(v);
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x141>(v));
+  v = fmaxf(v, dpp<0x140>(v));
+  return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)), fmaxf(lane_value(v, 32), lane_value(v, 48)));
 }
 
 // 8 bf16 weights (one lane's share of a unit) dotted with 8 fp32 activations in LDS.
@@ -145,7 +162,15 @@ struct Ctx {
   float* red;         // [kWaves] scratch
   uint64_t* red64;    // [kWaves]
   int* flags;         // [0] abort seen, [1] last-arriver, [2] token
+  float* part;        // [kMaxItems] partial sums of split items
+  uint64_t* tr;       // trace record of the current stage, or null
+  float rs;           // RMSNorm scale of the staged activation (1 if none)
 };
+
+// Trace stamp k of the current (workgroup, stage) record.
+__device__ __forceinline__ void mark(Ctx& c, int k) {
+  if (c.tr != nullptr && c.tid == 0) c.tr[k] = wall_clock64();
+}
 
 // Latch the first device error; a timeout also stops every workgroup.
 __device__ __forceinline__ void latch_error(const Params& P, int code, int stage, uint32_t detail) {
@@ -175,46 +200,81 @@ __device__ __forceinline__ bool poll_stop(const Params& P, uint64_t& t0, int sta
   return ld_u32_agent(P.abort_flag) != 0;
 }
 
-// Copy n tagged elements into LDS as fp32 once every one carries this step's
-// tag, and zero dst[n, zero_to).  WG-cooperative.  The first round of polls is
-// issued before a barrier that separates these LDS writes from the previous
-// task's last LDS reads, so the poll latency overlaps slower waves finishing.
-// Ends with a barrier.  Returns false if the wait was aborted.
-__device__ __forceinline__ bool stage_tagged(const Params& P, Ctx& c, float* dst, const uint64_t* src, int n, int stage,
-                                             int zero_to = 0) {
-  bool stop = false;
-  for (int i0 = 0; i0 == 0 || i0 < n; i0 += kThreads * 4) {
-    uint64_t w[4];
+// A run of tagged elements to stage into LDS: dst[i] = value(src[i]) * scale.
+struct Seg {
+  float* dst;
+  const uint64_t* src;
+  int n;
+  float scale;
+};
+
+constexpr int kStageLoads = 8;  // tagged loads per thread issued in one round
+
+// Copy tagged segments into LDS as fp32 once every element carries this
+// step's tag, and zero zdst[zfrom, zto).  WG-cooperative.  All loads of a
+// round are issued before any is checked, and the first round's loads are in
+// flight before the barrier that separates these LDS writes from the previous
+// task's last LDS reads.  Ends with a barrier; false if the wait was aborted.
+// Source element of flat index i over the segments (null past the end).
+template <int NSEG>
+__device__ __forceinline__ const uint64_t* seg_src(const Seg (&seg)[NSEG], int i) {
+  const uint64_t* r = nullptr;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = i0 + j * kThreads + c.tid;
-      w[j] = i < n ? ld_tag(src + i) : ((uint64_t)c.epoch << 32);
+  for (int k = 0; k < NSEG; ++k) {
+    if (i >= 0 && i < seg[k].n) r = seg[k].src + i;
+    i -= seg[k].n;
+  }
+  return r;
+}
+
+// Store the value of flat index i into its segment's LDS destination.
+template <int NSEG>
+__device__ __forceinline__ void seg_store(const Seg (&seg)[NSEG], int i, uint64_t w) {
+#pragma unroll
+  for (int k = 0; k < NSEG; ++k) {
+    if (i >= 0 && i < seg[k].n) seg[k].dst[i] = __uint_as_float((uint32_t)w) * seg[k].scale;
+    i -= seg[k].n;
+  }
+}
+
+template <int NSEG>
+__device__ __forceinline__ bool stage_tagged(const Params& P, Ctx& c, const Seg (&seg)[NSEG], int stage,
+                                             float* zdst = nullptr, int zfrom = 0, int zto = 0) {
+  int total = 0;
+#pragma unroll
+  for (int k = 0; k < NSEG; ++k) total += seg[k].n;
+  bool stop = false;
+  for (int i0 = 0; i0 == 0 || i0 < total; i0 += kThreads * kStageLoads) {
+    uint64_t w[kStageLoads];
+#pragma unroll
+    for (int j = 0; j < kStageLoads; ++j) {
+      const uint64_t* p = seg_src(seg, i0 + j * kThreads + c.tid);
+      w[j] = p ? ld_tag(p) : ((uint64_t)c.epoch << 32);
     }
     uint64_t t0 = 0;
     while (!stop) {
       bool ready = true;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) ready &= (uint32_t)(w[j] >> 32) == c.epoch;
+      for (int j = 0; j < kStageLoads; ++j) ready &= (uint32_t)(w[j] >> 32) == c.epoch;
       if (ready) break;
       if (poll_stop(P, t0, stage, (uint32_t)(w[0] >> 32))) {
         stop = true;
         break;
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = i0 + j * kThreads + c.tid;
-        if (i < n && (uint32_t)(w[j] >> 32) != c.epoch) w[j] = ld_tag(src + i);
+      for (int j = 0; j < kStageLoads; ++j) {
+        if ((uint32_t)(w[j] >> 32) != c.epoch) {
+          const uint64_t* p = seg_src(seg, i0 + j * kThreads + c.tid);
+          if (p) w[j] = ld_tag(p);
+        }
       }
     }
     if (i0 == 0) {
       __syncthreads();
-      for (int i = n + c.tid; i < zero_to; i += kThreads) dst[i] = 0.f;
+      for (int i = zfrom + c.tid; i < zto; i += kThreads) zdst[i] = 0.f;
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = i0 + j * kThreads + c.tid;
-      if (i < n) dst[i] = __uint_as_float((uint32_t)w[j]);
-    }
+    for (int j = 0; j < kStageLoads; ++j) seg_store(seg, i0 + j * kThreads + c.tid, w[j]);
   }
   if (stop) c.flags[0] = 1;
   __syncthreads();
@@ -233,45 +293,97 @@ __device__ __forceinline__ float block_sum(Ctx& c, float v) {
   return t;
 }
 
-// Embedding row of the input token (bf16 -> fp32) into dst[0, H).
-__device__ __forceinline__ void stage_embedding(const Params& P, Ctx& c, float* dst, int stage) {
-  if (c.tid == 0) {
-    int tok = P.token[0];
-    if (tok < 0 || tok >= P.V) {
-      latch_error(P, MK_E_TOKEN, stage, (uint32_t)tok);
-      __hip_atomic_store(&P.tokerr[0], c.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      tok = 0;
+// Stage the input x of an RMSNorm into LDS as dst[i] = x[i] * g[i] (i < n),
+// zero dst[n, npad), and set c.rs = (mean(x^2) + eps)^(-1/2), so that
+// W . rmsnorm(x) = c.rs * (W . dst).  x is either tagged (src) or, for the
+// first layer, the bf16 embedding row of the input token (src == null).  The
+// sum of squares is reduced under the barrier that ends the staging.
+// WG-cooperative; false if the wait was aborted.
+__device__ __forceinline__ bool stage_normed(const Params& P, Ctx& c, float* dst, const uint64_t* src, const float* g,
+                                             int n, int npad, int stage) {
+  const uint16_t* emb = nullptr;
+  if (src == nullptr) {
+    if (c.tid == 0) {
+      int tok = P.token[0];
+      if (tok < 0 || tok >= P.V) {
+        latch_error(P, MK_E_TOKEN, stage, (uint32_t)tok);
+        __hip_atomic_store(&P.tokerr[0], c.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        tok = 0;
+      }
+      c.flags[2] = tok;
     }
-    c.flags[2] = tok;
+    __syncthreads();
+    emb = P.embed + (size_t)c.flags[2] * P.H;
   }
-  __syncthreads();
-  const uint16_t* row = P.embed + (size_t)c.flags[2] * P.H;
-  for (int i = c.tid; i < P.H; i += kThreads) dst[i] = bf16_to_f32(row[i]);
-  __syncthreads();
-}
-
-// dst[0, n) = RMSNorm(dst) * g over the first n entries; dst[n, npad) = 0.
-__device__ __forceinline__ void rmsnorm_lds(const Params& P, Ctx& c, float* x, const float* g, int n, int npad) {
+  const uint64_t ready_tag = (uint64_t)c.epoch << 32;
   float ss = 0.f;
-  for (int i = c.tid; i < n; i += kThreads) ss = fmaf(x[i], x[i], ss);
-  ss = block_sum(c, ss);
-  const float r = rsqrtf(ss / (float)n + P.eps);
-  for (int i = c.tid; i < npad; i += kThreads) x[i] = i < n ? x[i] * r * g[i] : 0.f;
+  bool stop = false;
+  for (int i0 = 0; i0 == 0 || i0 < n; i0 += kThreads * kStageLoads) {
+    uint64_t w[kStageLoads];
+    float gv[kStageLoads];
+    if (emb) {
+      // in-bounds loads for every lane first (clamped index), then widen
+      uint32_t e16[kStageLoads];
+#pragma unroll
+      for (int j = 0; j < kStageLoads; ++j) {
+        const int i = i0 + j * kThreads + c.tid;
+        gv[j] = g[i < n ? i : n - 1];
+        e16[j] = emb[i < n ? i : n - 1];
+      }
+#pragma unroll
+      for (int j = 0; j < kStageLoads; ++j) w[j] = ready_tag | (uint64_t)(e16[j] << 16);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kStageLoads; ++j) {
+        const int i = i0 + j * kThreads + c.tid;
+        gv[j] = g[i < n ? i : n - 1];
+        w[j] = i < n ? ld_tag(src + i) : ready_tag;
+      }
+    }
+    uint64_t t0 = 0;
+    while (!stop) {
+      bool ready = true;
+#pragma unroll
+      for (int j = 0; j < kStageLoads; ++j) ready &= (uint32_t)(w[j] >> 32) == c.epoch;
+      if (ready) break;
+      if (poll_stop(P, t0, stage, (uint32_t)(w[0] >> 32))) {
+        stop = true;
+        break;
+      }
+#pragma unroll
+      for (int j = 0; j < kStageLoads; ++j) {
+        const int i = i0 + j * kThreads + c.tid;
+        if (i < n && (uint32_t)(w[j] >> 32) != c.epoch) w[j] = ld_tag(src + i);
+      }
+    }
+    if (i0 == 0) {
+      __syncthreads();
+      for (int i = n + c.tid; i < npad; i += kThreads) dst[i] = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kStageLoads; ++j) {
+      const int i = i0 + j * kThreads + c.tid;
+      if (i < n) {
+        const float x = __uint_as_float((uint32_t)w[j]);
+        ss = fmaf(x, x, ss);
+        dst[i] = x * gv[j];
+      }
+    }
+  }
+  ss = wave_sum(ss);
+  if (c.lane == 0) c.red[c.wave] = ss;
+  if (stop) c.flags[0] = 1;
   __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) t += c.red[w];
+  c.rs = rsqrtf(t / (float)n + P.eps);
+  return c.flags[0] == 0;
 }
 
 // ---------------------------------------------------------------------------
 // the per-wave weight stream (LDS ring, loader running ahead of the consumer)
 // ---------------------------------------------------------------------------
-
-struct Stream {
-  uint32_t ring;   // LDS byte address of this wave's ring
-  int issued, consumed, lslot, cslot;
-  int ls, s_end;
-  uint32_t lpair, lend, lnu, lu;
-  const char* lbase;
-  bool ldone;
-};
 
 // Task records are immutable during a launch; read them with a scalar load so
 // that neither the loader nor the consumer waits on vector-memory counters.
@@ -289,21 +401,36 @@ __device__ __forceinline__ Task task_at(const Params& P, int s, int b) {
   t.nu = r[3];
   t.wofs = (uint64_t)r[4] | ((uint64_t)r[5] << 32);
   t.ntasks = r[6];
-  t.pad = r[7];
+  t.kslog = r[7];
   return t;
 }
+
+// Work items of a GEMV task for one wave: items wave, wave+8, ... of
+// (a1 - a0) << kslog; item i is pair a0 + (i >> kslog), units
+// [(i & (2^kslog - 1)) * upi, + upi) of that pair, upi = nu >> kslog.
+struct Stream {
+  uint32_t ring;  // LDS byte address of this wave's ring
+  int issued, consumed, lslot, cslot;
+  int ls, s_end;
+  uint32_t litem, lnitems, lkslog, lupi, lu, la0, lnu;
+  const char* lbase;
+  bool ldone;
+};
 
 __device__ __forceinline__ void loader_seek(const Params& P, Stream& st, int s, int b, int wave) {
   for (; s < st.s_end; ++s) {
     const Task t = task_at(P, s, b);
     if (op_is_gemv(t.op)) {
-      const uint32_t p = t.a0 + (uint32_t)wave;
-      if (p < t.a1) {
+      const uint32_t n_items = (t.a1 - t.a0) << t.kslog;
+      if ((uint32_t)wave < n_items) {
         st.ls = s;
-        st.lpair = p;
-        st.lend = t.a1;
-        st.lnu = t.nu;
+        st.litem = (uint32_t)wave;
+        st.lnitems = n_items;
+        st.lkslog = t.kslog;
+        st.lupi = t.nu >> t.kslog;
         st.lu = 0;
+        st.la0 = t.a0;
+        st.lnu = t.nu;
         st.lbase = (t.region ? P.lm : P.arena) + t.wofs;
         return;
       }
@@ -315,14 +442,16 @@ __device__ __forceinline__ void loader_seek(const Params& P, Stream& st, int s, 
 
 __device__ __forceinline__ void loader_issue(const Params& P, Stream& st, int b, int wave, int lane) {
   if (st.ldone) return;
-  const char* g = st.lbase + ((uint64_t)st.lpair * st.lnu + st.lu) * kUnitBytes + (uint32_t)lane * 16u;
+  const uint32_t pair = st.la0 + (st.litem >> st.lkslog);
+  const uint32_t unit = (st.litem & ((1u << st.lkslog) - 1u)) * st.lupi + st.lu;
+  const char* g = st.lbase + ((uint64_t)pair * st.lnu + unit) * kUnitBytes + (uint32_t)lane * 16u;
   dma_unit(g, st.ring + (uint32_t)st.lslot * kUnitBytes);
   ++st.issued;
   st.lslot = (st.lslot + 1 == kRing) ? 0 : st.lslot + 1;
-  if (++st.lu == st.lnu) {
+  if (++st.lu == st.lupi) {
     st.lu = 0;
-    st.lpair += kWaves;
-    if (st.lpair >= st.lend) loader_seek(P, st, st.ls + 1, b, wave);
+    st.litem += kWaves;
+    if (st.litem >= st.lnitems) loader_seek(P, st, st.ls + 1, b, wave);
   }
 }
 
@@ -341,10 +470,10 @@ __device__ __forceinline__ uint4 consume_unit(const Params& P, Stream& st, int b
 }
 
 // ---------------------------------------------------------------------------
-// GEMV stages: prologue (stage activation), row pairs, epilogue
+// GEMV stages: prologue (stage activation), items, epilogue
 // ---------------------------------------------------------------------------
 
-// Residual input of layer l (x after the previous layer, or the embedding).
+// Residual input of layer l >= 1 (x after the previous layer).
 __device__ __forceinline__ const uint64_t* x_in(const Params& P, int l) {
   return P.x_ffn + (size_t)(l - 1) * P.H;
 }
@@ -352,29 +481,27 @@ __device__ __forceinline__ const uint64_t* x_in(const Params& P, int l) {
 template <int OP>
 __device__ __forceinline__ bool gemv_prologue(const Params& P, Ctx& c, const Task& t, int s) {
   const int l = t.layer;
+  c.rs = 1.f;
   if (OP == OP_QKV || OP == OP_LM) {
     const float* g = OP == OP_QKV ? P.g_attn + (size_t)l * P.Hp : P.g_final;
-    if (l == 0) {
-      stage_embedding(P, c, c.act, s);
-    } else if (!stage_tagged(P, c, c.act, x_in(P, l), P.H, s)) {
-      return false;
-    }
-    rmsnorm_lds(P, c, c.act, g, P.H, P.Hp);
+    // this position's cos/sin do not depend on the wait: load them first
+    float rv = 0.f;
+    if (OP == OP_QKV && c.tid < P.D) rv = P.rope[(size_t)c.pos * P.D + c.tid];
+    if (!stage_normed(P, c, c.act, l == 0 ? nullptr : x_in(P, l), g, P.H, P.Hp, s)) return false;
     if (OP == OP_QKV) {
-      const float* rp = P.rope + (size_t)c.pos * P.D;
-      for (int i = c.tid; i < P.D; i += kThreads) c.rope[i] = rp[i];
+      if (c.tid < P.D) c.rope[c.tid] = rv;
       __syncthreads();
     }
   } else if (OP == OP_GU) {
-    if (!stage_tagged(P, c, c.act, P.x_attn + (size_t)l * P.H, P.H, s)) return false;
-    rmsnorm_lds(P, c, c.act, P.g_ffn + (size_t)l * P.Hp, P.H, P.Hp);
+    if (!stage_normed(P, c, c.act, P.x_attn + (size_t)l * P.H, P.g_ffn + (size_t)l * P.Hp, P.H, P.Hp, s)) return false;
   } else {  // OPROJ, DOWN: plain activation + residual rows of this task
     const int n = OP == OP_OPROJ ? P.QD : P.F;
     const int np = OP == OP_OPROJ ? P.QDp : P.Fp;
     const uint64_t* src = OP == OP_OPROJ ? P.o + (size_t)l * P.QD : P.h + (size_t)l * P.F;
-    if (!stage_tagged(P, c, c.act, src, n, s, np)) return false;
     const int r0 = 2 * (int)t.a0, nr = 2 * (int)(t.a1 - t.a0);
     if (OP == OP_OPROJ && l == 0) {
+      const Seg seg[1] = {{c.act, src, n, 1.f}};
+      if (!stage_tagged(P, c, seg, s, c.act, n, np)) return false;
       // the residual of layer 0 is the embedding row itself
       if (c.tid == 0) {
         int tok = P.token[0];
@@ -387,7 +514,8 @@ __device__ __forceinline__ bool gemv_prologue(const Params& P, Ctx& c, const Tas
       __syncthreads();
     } else {
       const uint64_t* rs = OP == OP_OPROJ ? x_in(P, l) + r0 : P.x_attn + (size_t)l * P.H + r0;
-      if (!stage_tagged(P, c, c.res, rs, nr, s)) return false;
+      const Seg seg[2] = {{c.act, src, n, 1.f}, {c.res, rs, nr, 1.f}};
+      if (!stage_tagged(P, c, seg, s, c.act, n, np)) return false;
     }
   }
   return true;
@@ -398,12 +526,18 @@ struct LmBest {
   int i;
 };
 
+// Outputs of row pair `pair` (rows 2*pair, 2*pair+1) with dot products v0, v1.
+// w0 / w1: this thread writes the outputs that belong to row 0 / row 1.
 template <int OP>
 __device__ __forceinline__ void gemv_epilogue(const Params& P, Ctx& c, const Task& t, uint32_t pair, float v0, float v1,
-                                              LmBest& best) {
+                                              LmBest& best, bool w0, bool w1) {
   const int l = t.layer;
   const int r = 2 * (int)pair;
   const uint32_t tag = c.epoch;
+  if (OP == OP_QKV || OP == OP_GU || OP == OP_LM) {
+    v0 *= c.rs;
+    v1 *= c.rs;
+  }
   if (OP == OP_QKV) {
     if (r < P.QD + P.KVD) {  // q or k rows: rotate the pair (2i, 2i+1) of its head
       const int rr = r < P.QD ? r : r - P.QD;
@@ -412,40 +546,40 @@ __device__ __forceinline__ void gemv_epilogue(const Params& P, Ctx& c, const Tas
       const float y0 = v0 * cs - v1 * sn;
       const float y1 = v0 * sn + v1 * cs;
       if (r < P.QD) {
-        if (c.lane == 0) st_tag(P.q + (size_t)l * P.QD + r, y0, tag);
-        if (c.lane == 1) st_tag(P.q + (size_t)l * P.QD + r + 1, y1, tag);
+        if (w0) st_tag(P.q + (size_t)l * P.QD + r, y0, tag);
+        if (w1) st_tag(P.q + (size_t)l * P.QD + r + 1, y1, tag);
       } else {
         const uint16_t k0 = f32_to_bf16(y0), k1 = f32_to_bf16(y1);
         const int hk = rr / P.D;
-        if (c.lane == 0) {
+        if (w0) {
           uint16_t* dst = P.kcache + (((size_t)l * P.NKV + hk) * P.S + c.pos) * P.D + j;
           *reinterpret_cast<uint32_t*>(dst) = (uint32_t)k0 | ((uint32_t)k1 << 16);
           st_tag(P.kvcur + (size_t)l * 2 * P.KVD + rr, bf16_to_f32(k0), tag);
         }
-        if (c.lane == 1) st_tag(P.kvcur + (size_t)l * 2 * P.KVD + rr + 1, bf16_to_f32(k1), tag);
+        if (w1) st_tag(P.kvcur + (size_t)l * 2 * P.KVD + rr + 1, bf16_to_f32(k1), tag);
       }
     } else {  // v rows
       const int rr = r - P.QD - P.KVD;
       const int hv = rr / P.D, j = rr % P.D;
       const uint16_t b0 = f32_to_bf16(v0), b1 = f32_to_bf16(v1);
-      if (c.lane == 0) {
+      if (w0) {
         uint16_t* dst = P.vcache + (((size_t)l * P.NKV + hv) * P.S + c.pos) * P.D + j;
         *reinterpret_cast<uint32_t*>(dst) = (uint32_t)b0 | ((uint32_t)b1 << 16);
         st_tag(P.kvcur + ((size_t)l * 2 + 1) * P.KVD + rr, bf16_to_f32(b0), tag);
       }
-      if (c.lane == 1) st_tag(P.kvcur + ((size_t)l * 2 + 1) * P.KVD + rr + 1, bf16_to_f32(b1), tag);
+      if (w1) st_tag(P.kvcur + ((size_t)l * 2 + 1) * P.KVD + rr + 1, bf16_to_f32(b1), tag);
     }
   } else if (OP == OP_OPROJ || OP == OP_DOWN) {
     uint64_t* dst = (OP == OP_OPROJ ? P.x_attn : P.x_ffn) + (size_t)l * P.H + r;
     const int k = r - 2 * (int)t.a0;
-    if (c.lane == 0) st_tag(dst, c.res[k] + v0, tag);
-    if (c.lane == 1) st_tag(dst + 1, c.res[k + 1] + v1, tag);
+    if (w0) st_tag(dst, c.res[k] + v0, tag);
+    if (w1) st_tag(dst + 1, c.res[k + 1] + v1, tag);
   } else if (OP == OP_GU) {
     // pair = (gate row f, up row f): h_f = silu(gate) * up
     const float sg = v0 / (1.0f + __expf(-v0));
-    if (c.lane == 0) st_tag(P.h + (size_t)l * P.F + pair, sg * v1, tag);
+    if (w0) st_tag(P.h + (size_t)l * P.F + pair, sg * v1, tag);
   } else if (OP == OP_LM) {
-    if (c.lane == 0) {
+    if (w0) {
       P.logits[r] = v0;
       P.logits[r + 1] = v1;
     }
@@ -490,132 +624,232 @@ __device__ __forceinline__ void lm_finish(const Params& P, Ctx& c, const Task& t
 template <int OP>
 __device__ __forceinline__ bool gemv_task(const Params& P, Ctx& c, Stream& st, const Task& t, int s) {
   if (!gemv_prologue<OP>(P, c, t, s)) return false;
-  const int half = (int)t.nu >> 1;  // units per row
+  mark(c, 1);
   LmBest best{-__builtin_inff(), -1};
   const float* xa = c.act + c.lane * 8;
-  for (uint32_t pair = t.a0 + (uint32_t)c.wave; pair < t.a1; pair += kWaves) {
-    float a0 = 0.f, a1 = 0.f;
-    for (int j = 0; j < half; ++j) a0 += dot8(consume_unit(P, st, c.b, c.wave, c.lane), xa + j * kUnitElems);
-    for (int j = 0; j < half; ++j) a1 += dot8(consume_unit(P, st, c.b, c.wave, c.lane), xa + j * kUnitElems);
-    a0 = wave_sum(a0);
-    a1 = wave_sum(a1);
-    gemv_epilogue<OP>(P, c, t, pair, a0, a1, best);
+  if (t.kslog == 0) {
+    // whole pairs per wave; the wave finishes each pair
+    const int half = (int)t.nu >> 1;  // units per row
+    for (uint32_t pair = t.a0 + (uint32_t)c.wave; pair < t.a1; pair += kWaves) {
+      float a0 = 0.f, a1 = 0.f;
+      for (int j = 0; j < half; ++j) a0 += dot8(consume_unit(P, st, c.b, c.wave, c.lane), xa + j * kUnitElems);
+      for (int j = 0; j < half; ++j) a1 += dot8(consume_unit(P, st, c.b, c.wave, c.lane), xa + j * kUnitElems);
+      a0 = wave_sum(a0);
+      a1 = wave_sum(a1);
+      gemv_epilogue<OP>(P, c, t, pair, a0, a1, best, c.lane == 0, c.lane == 1);
+    }
+  } else {
+    // split items: row segments spread over all waves, partials added in LDS
+    const uint32_t ks = 1u << t.kslog, hks = ks >> 1;
+    const int upi = (int)(t.nu >> t.kslog);
+    const uint32_t n_items = (t.a1 - t.a0) << t.kslog;
+    for (uint32_t i = (uint32_t)c.wave; i < n_items; i += kWaves) {
+      const int col = (int)(i & (hks - 1u)) * upi;  // first unit of the item inside its row
+      float a = 0.f;
+      for (int j = 0; j < upi; ++j) a += dot8(consume_unit(P, st, c.b, c.wave, c.lane), xa + (col + j) * kUnitElems);
+      a = wave_sum(a);
+      if (c.lane == 0) c.part[i] = a;
+    }
+    __syncthreads();
+    for (uint32_t pl = (uint32_t)c.tid; pl < t.a1 - t.a0; pl += kThreads) {
+      float v0 = 0.f, v1 = 0.f;
+      for (uint32_t k = 0; k < hks; ++k) v0 += c.part[pl * ks + k];
+      for (uint32_t k = hks; k < ks; ++k) v1 += c.part[pl * ks + k];
+      gemv_epilogue<OP>(P, c, t, t.a0 + pl, v0, v1, best, true, true);
+    }
   }
+  mark(c, 2);
   if (OP == OP_LM) lm_finish(P, c, t, best);
   return true;
 }
 
 // ---------------------------------------------------------------------------
-// attention: one (kv head, chunk) per task, G query heads, merge by last chunk
+// attention: one (kv head, chunk) per task, G query heads of D dims
 // ---------------------------------------------------------------------------
 
-template <int G>
+// Scores: thread i < len owns position t0 + i and dots the whole K row with
+// the G queries (no cross-lane sum).  P.V: wave w owns positions t0 + w + 8j
+// and lane l owns dims [l * D/64, (l+1) * D/64); the eight waves' partial sums
+// are added in LDS in wave order.  The K row of each score thread and the V
+// values of each P.V lane are read before the task waits for this step's q, k
+// and v: every slot below pos was written by an earlier step.
+template <int G, int D>
 __device__ __forceinline__ bool attn_task(const Params& P, Ctx& c, const Task& t, int s) {
+  constexpr int NV = kMaxChunk / kWaves;  // P.V positions per wave
+  constexpr int DPL = D / 64;             // P.V dims per lane
   const int l = t.layer, g = (int)t.a0, ch = (int)t.a1;
-  const int D = P.D, C = P.attn_chunks;
+  const int C = P.attn_chunks;
   const int n = c.pos + 1;
-  const int len = (n + C - 1) / C;
-  const int t0 = min(n, ch * len), t1 = min(n, t0 + len);
-  const int lmax = (P.S + C - 1) / C;
-  const int NP = kThreads / D;
-  float* qs = c.act;             // [G][D]
-  float* kcur = qs + G * D;      // [D]
-  float* vcur = kcur + D;        // [D]
-  float* sc = vcur + D;          // [lmax][G]
-  float* part = sc + lmax * G;   // [NP][G][D]
-  float* red = part + NP * G * D;  // m[kMaxGroup], l[kMaxGroup]
-
-  if (!stage_tagged(P, c, qs, P.q + (size_t)l * P.QD + (size_t)g * G * D, G * D, s)) return false;
-  if (!stage_tagged(P, c, kcur, P.kvcur + (size_t)l * 2 * P.KVD + (size_t)g * D, D, s)) return false;
-  if (!stage_tagged(P, c, vcur, P.kvcur + ((size_t)l * 2 + 1) * P.KVD + (size_t)g * D, D, s)) return false;
-  for (int i = c.tid; i < G * D; i += kThreads) qs[i] *= P.qscale;
-  __syncthreads();
+  const int len0 = (n + C - 1) / C;
+  const int t0 = min(n, ch * len0), t1 = min(n, t0 + len0);
+  const int len = t1 - t0;
 
   const size_t head_off = ((size_t)l * P.NKV + g) * P.S * D;
   const uint16_t* kc = P.kcache + head_off;
   const uint16_t* vc = P.vcache + head_off;
+  // TPP threads per score position, each over 64 of the D dims
+  constexpr int TPP = D / 64;
+  const int sp = c.tid / TPP;            // position slot of this thread
+  const int dq = (c.tid % TPP) * 64;     // first dim of this thread
+  const int ts = t0 + sp;
+  const bool scorer = sp < len;
+  // Branch-free prefetch: every lane loads from an in-bounds slot (slot 0 when
+  // its own slot is out of range or is pos) and the raw bits are masked at
+  // use, so all loads issue back to back instead of one wait per load.
+  uint4 kr[8];
+  {
+    const int tk = (scorer && ts != c.pos) ? ts : 0;
+    const uint4* row = reinterpret_cast<const uint4*>(kc + (size_t)tk * D + dq);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) kr[q] = row[q];
+  }
+  uint32_t vv[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int tv = t0 + c.wave + kWaves * j;
+    const int tl = (tv < t1 && tv != c.pos) ? tv : 0;
+    if (DPL == 1)
+      vv[j] = vc[(size_t)tl * D + c.lane];
+    else
+      vv[j] = reinterpret_cast<const uint32_t*>(vc + (size_t)tl * D)[c.lane];
+  }
 
-  // scores s[t][h] = q_h . k_t / sqrt(D)
-  for (int tt = t0 + c.tid; tt < t1; tt += kThreads) {
-    float acc[G];
+  float* qs = c.act;                    // [G][D], pre-scaled by 1/sqrt(D)
+  float* kcur = qs + G * D;             // [D]
+  float* vcur = kcur + D;               // [D]
+  float* sc = vcur + D;                 // [kMaxChunk][G] scores, then probabilities
+  float* wpart = sc + kMaxChunk * G;    // [kWaves][G][D]
+  float* wm = wpart + kWaves * G * D;   // [kMaxGroup] per-head max
+  float* wl = wm + kMaxGroup;           // [kMaxGroup] per-head sum
+  {
+    const Seg seg[3] = {{qs, P.q + (size_t)l * P.QD + (size_t)g * G * D, G * D, P.qscale},
+                        {kcur, P.kvcur + (size_t)l * 2 * P.KVD + (size_t)g * D, D, 1.f},
+                        {vcur, P.kvcur + ((size_t)l * 2 + 1) * P.KVD + (size_t)g * D, D, 1.f}};
+    if (!stage_tagged(P, c, seg, s)) return false;
+  }
+  mark(c, 1);
+
+  // The row at pos came from this step's staged k and v; their values are
+  // bf16-exact, so they go back into the prefetch registers as bf16 bits and
+  // the loops below need no per-position branch.
+  if (scorer && ts == c.pos) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) acc[h] = 0.f;
-    if (tt == c.pos) {
-      for (int d = 0; d < D; ++d) {
-        const float kv = kcur[d];
-#pragma unroll
-        for (int h = 0; h < G; ++h) acc[h] = fmaf(qs[h * D + d], kv, acc[h]);
-      }
-    } else {
-      const uint4* row = reinterpret_cast<const uint4*>(kc + (size_t)tt * D);
-      for (int d8 = 0; d8 < D / 8; ++d8) {
-        const uint4 w = row[d8];
-        const float k8[8] = {bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y),
-                             bf_lo(w.z), bf_hi(w.z), bf_lo(w.w), bf_hi(w.w)};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-#pragma unroll
-          for (int h = 0; h < G; ++h) acc[h] = fmaf(qs[h * D + d8 * 8 + e], k8[e], acc[h]);
-        }
-      }
+    for (int q = 0; q < 8; ++q) {
+      const float* k = kcur + dq + q * 8;
+      kr[q].x = (__float_as_uint(k[0]) >> 16) | (__float_as_uint(k[1]) & 0xffff0000u);
+      kr[q].y = (__float_as_uint(k[2]) >> 16) | (__float_as_uint(k[3]) & 0xffff0000u);
+      kr[q].z = (__float_as_uint(k[4]) >> 16) | (__float_as_uint(k[5]) & 0xffff0000u);
+      kr[q].w = (__float_as_uint(k[6]) >> 16) | (__float_as_uint(k[7]) & 0xffff0000u);
     }
+  }
+  {
+    const uint32_t vcb = DPL == 1 ? (__float_as_uint(vcur[c.lane]) >> 16)
+                                  : ((__float_as_uint(vcur[2 * c.lane]) >> 16) |
+                                     (__float_as_uint(vcur[2 * c.lane + 1]) & 0xffff0000u));
 #pragma unroll
-    for (int h = 0; h < G; ++h) sc[(tt - t0) * G + h] = acc[h];
+    for (int j = 0; j < NV; ++j) {
+      const int tv = t0 + c.wave + kWaves * j;
+      vv[j] = tv == c.pos ? vcb : vv[j];
+    }
+  }
+
+  // heads are an outer, not unrolled loop: unrolling it would let the
+  // scheduler hoist every broadcast read of q into registers at once
+#pragma unroll 1
+  for (int h = 0; h < G; ++h) {
+    float a = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint4 w = kr[q];
+      const float4 qa = *reinterpret_cast<const float4*>(qs + h * D + dq + q * 8);
+      const float4 qb = *reinterpret_cast<const float4*>(qs + h * D + dq + q * 8 + 4);
+      a = fmaf(qa.x, bf_lo(w.x), a); a = fmaf(qa.y, bf_hi(w.x), a);
+      a = fmaf(qa.z, bf_lo(w.y), a); a = fmaf(qa.w, bf_hi(w.y), a);
+      a = fmaf(qb.x, bf_lo(w.z), a); a = fmaf(qb.y, bf_hi(w.z), a);
+      a = fmaf(qb.z, bf_lo(w.w), a); a = fmaf(qb.w, bf_hi(w.w), a);
+    }
+    if (TPP == 2) a += dpp<0xB1>(a);  // the two halves of the position's dims (adjacent lanes)
+    if (scorer && (c.tid % TPP) == 0) sc[sp * G + h] = a;
   }
   __syncthreads();
 
-  // per-head max and exp-sum of this chunk (wave h owns head h)
+  // softmax statistics of this chunk: wave h owns head h
   if (c.wave < G) {
     const int h = c.wave;
     float m = -__builtin_inff();
-    for (int i = c.lane; i < t1 - t0; i += 64) m = fmaxf(m, sc[i * G + h]);
+    for (int i = c.lane; i < len; i += 64) m = fmaxf(m, sc[i * G + h]);
     m = wave_max(m);
     float ls = 0.f;
-    for (int i = c.lane; i < t1 - t0; i += 64) {
+    for (int i = c.lane; i < len; i += 64) {
       const float p = __expf(sc[i * G + h] - m);
       sc[i * G + h] = p;
       ls += p;
     }
     ls = wave_sum(ls);
     if (c.lane == 0) {
-      red[h] = m;
-      red[kMaxGroup + h] = ls;
+      wm[h] = m;
+      wl[h] = ls;
     }
   }
   __syncthreads();
 
-  // acc[h][d] = sum_t p[t][h] v_t[d], positions split over NP partitions
-  {
-    const int d = c.tid % D, prt = c.tid / D;
-    float acc[G];
+  float acc[G][DPL];
 #pragma unroll
-    for (int h = 0; h < G; ++h) acc[h] = 0.f;
-    for (int tt = t0 + prt; tt < t1; tt += NP) {
-      const float v = tt == c.pos ? vcur[d] : bf16_to_f32(vc[(size_t)tt * D + d]);
+  for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int h = 0; h < G; ++h) acc[h] = fmaf(sc[(tt - t0) * G + h], v, acc[h]);
+    for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int tv = t0 + c.wave + kWaves * j;
+    const bool live = tv < t1;
+    const int slot = live ? tv - t0 : 0;  // in-bounds read, masked below
+    float v[DPL];
+    v[0] = bf_lo(vv[j]);
+    if (DPL == 2) v[DPL - 1] = bf_hi(vv[j]);
+    float pr[G];
+    if (G == 4) {
+      const float4 q4 = *reinterpret_cast<const float4*>(sc + slot * G);
+      pr[0] = q4.x; pr[G > 1 ? 1 : 0] = q4.y; pr[G > 2 ? 2 : 0] = q4.z; pr[G > 3 ? 3 : 0] = q4.w;
+    } else if (G == 2) {
+      const float2 q2 = *reinterpret_cast<const float2*>(sc + slot * G);
+      pr[0] = q2.x; pr[G > 1 ? 1 : 0] = q2.y;
+    } else {
+      pr[0] = sc[slot * G];
     }
 #pragma unroll
-    for (int h = 0; h < G; ++h) part[(prt * G + h) * D + d] = acc[h];
+    for (int h = 0; h < G; ++h) {
+      const float p = live ? pr[h] : 0.f;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[h][e] = fmaf(p, v[e], acc[h][e]);
+    }
   }
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) wpart[(c.wave * G + h) * D + c.lane * DPL + e] = acc[h][e];
   __syncthreads();
+  mark(c, 2);
 
   const int h = c.tid / D, d = c.tid % D;
-  float a = 0.f;
-  if (c.tid < G * D)
-    for (int p = 0; p < NP; ++p) a += part[(p * G + h) * D + d];
+  float a = 0.f, lh = 0.f, mh = 0.f;
+  if (c.tid < G * D) {
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) a += wpart[(w * G + h) * D + d];
+    lh = wl[h];
+    mh = wm[h];
+  }
   uint64_t* o = P.o + (size_t)l * P.QD + (size_t)g * G * D;
   if (C == 1) {
-    if (c.tid < G * D) st_tag(o + c.tid, a / red[kMaxGroup + h], c.epoch);
+    if (c.tid < G * D) st_tag(o + c.tid, a / lh, c.epoch);
     return true;
   }
   // publish this chunk's partial {m[G], l[G], acc[G][D]}; the last chunk of the head merges
   const int stride = G * (D + 2);
   float* mine = P.attn_part + (((size_t)l * P.NKV + g) * C + ch) * stride;
   if (c.tid < G * D) st_f32_agent(mine + 2 * G + c.tid, a);
-  if (c.tid < G) {
-    st_f32_agent(mine + c.tid, red[c.tid]);
-    st_f32_agent(mine + G + c.tid, red[kMaxGroup + c.tid]);
+  if (c.tid < G * D && d == 0) {
+    st_f32_agent(mine + h, mh);
+    st_f32_agent(mine + G + h, lh);
   }
   wait_all_vmem();
   __syncthreads();
@@ -646,6 +880,9 @@ __device__ __forceinline__ bool attn_task(const Params& P, Ctx& c, const Task& t
 // the stage loop shared by the persistent kernel and the per-stage kernels
 // ---------------------------------------------------------------------------
 
+// G query heads per kv head and head_dim D are template parameters so that a
+// kernel instance carries exactly one attention variant (register budget).
+template <int G, int D>
 __device__ __forceinline__ void run_stages(const Params& P, int s_begin, int s_end) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   Ctx c;
@@ -666,7 +903,9 @@ __device__ __forceinline__ void run_stages(const Params& P, int s_begin, int s_e
   c.red = reinterpret_cast<float*>(smem + P.lds_misc);
   c.red64 = reinterpret_cast<uint64_t*>(smem + P.lds_misc + 64);
   c.flags = reinterpret_cast<int*>(smem + P.lds_misc + 128);
+  c.part = reinterpret_cast<float*>(smem + P.lds_part);
   if (c.tid < 4) c.flags[c.tid] = 0;
+  c.tr = nullptr;
   __syncthreads();
 
   Stream st;
@@ -679,6 +918,8 @@ __device__ __forceinline__ void run_stages(const Params& P, int s_begin, int s_e
 
   for (int s = s_begin; s < s_end; ++s) {
     const Task t = task_at(P, s, c.b);
+    c.tr = (P.trace != nullptr && t.op != OP_NONE) ? P.trace + ((size_t)c.b * P.num_stages + s) * 4 : nullptr;
+    mark(c, 0);
     bool ok = true;
     switch (t.op) {
       case OP_QKV: ok = gemv_task<OP_QKV>(P, c, st, t, s); break;
@@ -686,24 +927,24 @@ __device__ __forceinline__ void run_stages(const Params& P, int s_begin, int s_e
       case OP_GU: ok = gemv_task<OP_GU>(P, c, st, t, s); break;
       case OP_DOWN: ok = gemv_task<OP_DOWN>(P, c, st, t, s); break;
       case OP_LM: ok = gemv_task<OP_LM>(P, c, st, t, s); break;
-      case OP_ATTN:
-        switch (P.G) {
-          case 1: ok = attn_task<1>(P, c, t, s); break;
-          case 2: ok = attn_task<2>(P, c, t, s); break;
-          case 4: ok = attn_task<4>(P, c, t, s); break;
-          default: ok = attn_task<8>(P, c, t, s); break;
-        }
-        break;
+      case OP_ATTN: ok = attn_task<G, D>(P, c, t, s); break;
       default: break;
     }
+    mark(c, 3);
     if (!ok) break;
   }
   wait_all_vmem();
 }
 
-__global__ void __launch_bounds__(kThreads, 1) mk_persistent(Params P) { run_stages(P, 0, P.num_stages); }
+template <int G, int D>
+__global__ void __launch_bounds__(kThreads, 1) mk_persistent(Params P) {
+  run_stages<G, D>(P, 0, P.num_stages);
+}
 
-__global__ void __launch_bounds__(kThreads, 1) mk_stage(Params P, int s) { run_stages(P, s, s + 1); }
+template <int G, int D>
+__global__ void __launch_bounds__(kThreads, 1) mk_stage(Params P, int s) {
+  run_stages<G, D>(P, s, s + 1);
+}
 
 __global__ void mk_set_args(StepArgs* a, int pos, uint32_t epoch) {
   a->pos = pos;
@@ -719,27 +960,46 @@ __global__ void mk_advance_args(StepArgs* a) {
 // host-side launchers
 // ---------------------------------------------------------------------------
 
-hipError_t configure_kernels(int lds_bytes) {
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&mk_persistent),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
-  if (e != hipSuccess) return e;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&mk_stage), hipFuncAttributeMaxDynamicSharedMemorySize,
-                             lds_bytes);
+namespace {
+
+// Kernel instances for (G, D): G in {1, 2, 4}, D in {64, 128}.
+struct KernelPair {
+  const void* persistent;
+  const void* stage;
+};
+
+template <int G, int D>
+KernelPair pair_of() {
+  return {reinterpret_cast<const void*>(&mk_persistent<G, D>), reinterpret_cast<const void*>(&mk_stage<G, D>)};
 }
 
-hipError_t persistent_occupancy(int lds_bytes, int* blocks_per_cu) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, reinterpret_cast<const void*>(&mk_persistent),
-                                                      kThreads, lds_bytes);
+KernelPair kernels_for(int G, int D) {
+  if (D == 64) return G == 1 ? pair_of<1, 64>() : G == 2 ? pair_of<2, 64>() : pair_of<4, 64>();
+  return G == 1 ? pair_of<1, 128>() : G == 2 ? pair_of<2, 128>() : pair_of<4, 128>();
+}
+
+}  // namespace
+
+hipError_t configure_kernels(int G, int D, int lds_bytes) {
+  const KernelPair k = kernels_for(G, D);
+  hipError_t e = hipFuncSetAttribute(k.persistent, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute(k.stage, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+}
+
+hipError_t persistent_occupancy(int G, int D, int lds_bytes, int* blocks_per_cu) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, kernels_for(G, D).persistent, kThreads,
+                                                      lds_bytes);
 }
 
 hipError_t launch_persistent(const Params& P, int lds_bytes, hipStream_t stream) {
-  hipLaunchKernelGGL(mk_persistent, dim3(P.num_wgs), dim3(kThreads), lds_bytes, stream, P);
-  return hipGetLastError();
+  void* args[] = {const_cast<Params*>(&P)};
+  return hipLaunchKernel(kernels_for(P.G, P.D).persistent, dim3(P.num_wgs), dim3(kThreads), args, lds_bytes, stream);
 }
 
 hipError_t launch_stage(const Params& P, int s, int lds_bytes, hipStream_t stream) {
-  hipLaunchKernelGGL(mk_stage, dim3(P.num_wgs), dim3(kThreads), lds_bytes, stream, P, s);
-  return hipGetLastError();
+  void* args[] = {const_cast<Params*>(&P), &s};
+  return hipLaunchKernel(kernels_for(P.G, P.D).stage, dim3(P.num_wgs), dim3(kThreads), args, lds_bytes, stream);
 }
 
 hipError_t launch_set_args(StepArgs* a, int pos, uint32_t epoch, hipStream_t stream) {

@@ -24,6 +24,26 @@ int fail(Plan& p, int code, const char* msg) {
   return code;
 }
 
+// Split of each row pair into 2^k items so that the 8 waves of a workgroup
+// share `pairs` pairs of nu units evenly: minimise the units of the busiest
+// wave, prefer fewer splits on ties.  Items must stay inside one row.
+uint32_t split_log2(uint32_t pairs, uint32_t nu) {
+  uint32_t best = 0;
+  uint64_t best_cost = ~0ull;
+  for (uint32_t k = 0; (1u << k) <= nu; ++k) {
+    const uint32_t ks = 1u << k;
+    if (ks > 1 && ((nu / 2) % (ks / 2)) != 0) break;
+    if ((uint64_t)pairs * ks > (uint64_t)kMaxItems && ks > 1) break;
+    const uint64_t items = (uint64_t)pairs * ks;
+    const uint64_t cost = (items + kWaves - 1) / kWaves * (nu / ks);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = k;
+    }
+  }
+  return best;
+}
+
 }  // namespace
 
 uint64_t qkv_rows(const Plan& p) { return (uint64_t)p.QD + 2ull * p.KVD; }
@@ -34,10 +54,12 @@ int plan_build(const mk_config& c, int W, Plan& p) {
       c.vocab <= 0 || c.max_seq <= 0 || c.batch <= 0)
     return fail(p, MK_E_INVAL, "dimensions must be positive (n_layers >= 0)");
   if (c.n_heads % c.n_kv_heads != 0) return fail(p, MK_E_INVAL, "n_heads must be a multiple of n_kv_heads");
-  if (c.head_dim % 8 != 0 || kThreads % c.head_dim != 0)
-    return fail(p, MK_E_UNSUPPORTED, "head_dim must be a multiple of 8 dividing 512");
+  if (c.head_dim != 64 && c.head_dim != 128) return fail(p, MK_E_UNSUPPORTED, "head_dim must be 64 or 128");
   if (c.hidden % 2 != 0 || c.vocab % 2 != 0) return fail(p, MK_E_UNSUPPORTED, "hidden and vocab must be even");
-  if (c.n_heads / c.n_kv_heads > kMaxGroup) return fail(p, MK_E_UNSUPPORTED, "more than 8 query heads per kv head");
+  {
+    const int grp = c.n_heads / c.n_kv_heads;
+    if (grp != 1 && grp != 2 && grp != 4) return fail(p, MK_E_UNSUPPORTED, "1, 2 or 4 query heads per kv head");
+  }
   if (c.batch != 1) return fail(p, MK_E_UNSUPPORTED, "this build decodes batch 1");
   if (!(c.rms_eps >= 0.0f) || !(c.rope_theta > 0.0)) return fail(p, MK_E_INVAL, "rms_eps >= 0 and rope_theta > 0");
   if (c.exec_mode < MK_MODE_MEGA || c.exec_mode > MK_MODE_GRAPH) return fail(p, MK_E_INVAL, "unknown exec_mode");
@@ -61,14 +83,15 @@ int plan_build(const mk_config& c, int W, Plan& p) {
   p.QDp = round_up(p.QD, kRowAlign);
   p.Fp = round_up(p.F, kRowAlign);
 
-  // Attention split: chunks of at most 256 positions, at most one task per workgroup.
+  // Attention split: chunks of at most kMaxChunk positions, at most one task per workgroup.
   int C = c.attn_chunks;
-  if (C <= 0) C = (p.S + 255) / 256;
+  if (C <= 0) C = (p.S + kMaxChunk - 1) / kMaxChunk;
   C = std::max(1, std::min(C, p.S));
   if ((int64_t)C * p.NKV > W) C = std::max(1, W / p.NKV);
   if ((int64_t)C * p.NKV > W) return fail(p, MK_E_UNSUPPORTED, "more kv heads than workgroups");
   p.C = C;
   const int lmax = (p.S + C - 1) / C;  // longest chunk
+  if (lmax > kMaxChunk) return fail(p, MK_E_UNSUPPORTED, "attention chunk longer than 256 positions");
 
   // ---- packed arena layout: per layer [Wq;Wk;Wv] | Wo | [gate/up interleaved] | Wd
   const uint64_t align = 4096;
@@ -113,6 +136,7 @@ int plan_build(const mk_config& c, int W, Plan& p) {
       t.nu = nu;
       t.wofs = wofs;
       t.ntasks = n;
+      t.kslog = op == OP_LM ? 0u : split_log2((uint32_t)(a1 - a0), nu);
       if (op == OP_OPROJ || op == OP_DOWN) max_res_rows = std::max(max_res_rows, (int)(2 * (a1 - a0)));
     }
   };
@@ -137,15 +161,17 @@ int plan_build(const mk_config& c, int W, Plan& p) {
   for (const Task& t : p.tape) p.num_tasks += t.op != OP_NONE;
 
   // ---- LDS layout
-  const int np = kThreads / p.D;  // position partitions in the attention PV loop
-  const int attn_floats = p.G * p.D + 2 * p.D + lmax * p.G + np * p.G * p.D + 4 * kMaxGroup;
+  // attention scratch: q [G][D], k and v of this step [D] each, scores
+  // [kMaxChunk][G], per-wave partial outputs [waves][G][D], head max and sum
+  const int attn_floats = p.G * p.D + 2 * p.D + kMaxChunk * p.G + kWaves * p.G * p.D + 2 * kMaxGroup;
   p.act_floats = round_up(std::max(std::max(p.Hp, p.QDp), std::max(p.Fp, attn_floats)), 4);
   p.res_floats = round_up(std::max(max_res_rows, 4), 4);
   p.lds_act = kRingBytes;
   p.lds_res = p.lds_act + p.act_floats * 4;
   p.lds_rope = p.lds_res + p.res_floats * 4;
   p.lds_misc = p.lds_rope + round_up(p.D, 4) * 4;
-  p.lds_bytes = p.lds_misc + 256;
+  p.lds_part = p.lds_misc + 256;
+  p.lds_bytes = p.lds_part + kMaxItems * 4;
   if (p.lds_bytes > 160 * 1024) return fail(p, MK_E_UNSUPPORTED, "LDS plan exceeds 160 KiB per workgroup");
   return MK_OK;
 }
@@ -210,6 +236,12 @@ int plan_validate(const Plan& p, std::string* why) {
       if ((kind == OP_OPROJ || kind == OP_DOWN) && 2 * (t.a1 - t.a0) > (uint32_t)p.res_floats)
         return bad("residual rows exceed LDS");
       if (t.region != (kind == OP_LM ? 1 : 0)) return bad("weight region");
+      if (t.kslog > 0) {
+        const uint32_t ks = 1u << t.kslog;
+        if (kind == OP_LM) return bad("LM head is never split");
+        if ((t.nu / 2) % (ks / 2) != 0) return bad("split item crosses a row");
+        if ((uint64_t)(t.a1 - t.a0) * ks > (uint64_t)kMaxItems) return bad("too many split items");
+      }
     }
     if (next != pairs) return bad("row pairs not covered");
   }
