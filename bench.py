@@ -52,9 +52,9 @@ def cpu_cores() -> int:
         return os.cpu_count() or 1
 
 
-def time_mode(mk, torch, shape, wdev, mode, prompt, warmup, steps, max_seq, start_pos):
+def time_mode(mk, torch, shape, wdev, mode, prompt, warmup, steps, max_seq, start_pos, attn_chunks=0):
     """Prefill, warm up, then time `steps` chained greedy steps. Returns (ms/step, tokens)."""
-    eng = mk.Engine(shape, wdev, max_seq, mode=mode)
+    eng = mk.Engine(shape, wdev, max_seq, mode=mode, attn_chunks=attn_chunks)
     dims = (1, shape.n_layers, shape.n_kv_heads, max_seq, shape.head_dim)
     k = torch.zeros(dims, dtype=torch.int16, device="cuda")
     v = torch.zeros(dims, dtype=torch.int16, device="cuda")
@@ -102,7 +102,8 @@ def cpu_baseline(shape, weights, start_pos: int, budget_s: float = 12.0):
     from synth_inputs import make_kv_cache, make_start_token
 
     o = orc.Oracle(shape, weights)
-    kc, vc = make_kv_cache(shape, 1, start_pos + 64, start_pos, master=0)
+    cap = 1024
+    kc, vc = make_kv_cache(shape, 1, start_pos + cap, start_pos, master=0)
     kc, vc = kc[0], vc[0]
     tok = make_start_token(shape, 0)
     n = 0
@@ -111,7 +112,7 @@ def cpu_baseline(shape, weights, start_pos: int, budget_s: float = 12.0):
         lg = o.decode_step(tok, start_pos + n, kc, vc)
         tok = int(np.argmax(lg))
         n += 1
-        if (time.perf_counter() - t0 > budget_s and n >= 2) or n >= 64:
+        if (time.perf_counter() - t0 > budget_s and n >= 2) or n >= cap:
             break
     dt = time.perf_counter() - t0
     return {
@@ -125,6 +126,20 @@ def cpu_baseline(shape, weights, start_pos: int, budget_s: float = 12.0):
     }
 
 
+def copy_probe(mib: int) -> int:
+    """Plain copies of known size: their FETCH_SIZE / WRITE_SIZE per dispatch
+    against mib MiB give the factor that turns those counters into bytes."""
+    import torch
+
+    a = torch.ones(mib * (1 << 20) // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(4):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_mib": mib, "dispatches": 4}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -133,10 +148,16 @@ def main() -> int:
     ap.add_argument("--workload", default="llama1b")
     ap.add_argument("--modes", default="mega,graph,multi")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--attn-chunks", type=int, default=0, help="KV split per head (0: automatic)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="only run 4 device-to-device copies of this many MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the decode path runs on one GPU; multi-GPU runs are not supported, "
+                                   "use --gpus 1"}))
         return 2
+    if args.copy_mib > 0:
+        return copy_probe(args.copy_mib)
 
     import torch
 
@@ -160,7 +181,8 @@ def main() -> int:
     results = {}
     tokens = {}
     for mode in args.modes.split(","):
-        ms, toks = time_mode(mk, torch, shape, wdev, mode, prompt, args.warmup, steps, max_seq, start)
+        ms, toks = time_mode(mk, torch, shape, wdev, mode, prompt, args.warmup, steps, max_seq, start,
+                             args.attn_chunks)
         results[mode] = ms
         tokens[mode] = toks
         print(f"[bench] {mode}: {ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)

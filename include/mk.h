@@ -193,12 +193,14 @@ const char* mk_error_string(int code);
 
 /* mk_trace_copy -- wait for the device, then copy the trace of the latest
  * step into host memory out[capacity_words]: num_wgs * num_stages records of
- * four uint64 stamps {stage entered, inputs ready, compute done, stage left}
- * read from the device-wide constant-rate clock (s_memrealtime), record
- * (wg, stage) at word 4 * (wg * num_stages + stage); a stamp of 0 means the
- * workgroup had no task in that stage.  *words_written gets the word count and
- * *clock_khz the clock rate.  Errors: MK_E_INVAL (null, capacity too small,
- * handle loaded without cfg.trace), MK_E_HIP. */
+ * 20 uint64 stamps read from the device-wide constant-rate clock
+ * (s_memrealtime): {stage entered, inputs ready, compute done, stage left,
+ * then the time each of the 8 waves finished its own part, then the time each
+ * wave had its first weight unit of the task}; record (wg, stage) starts at
+ * word 20 * (wg * num_stages + stage), and a stamp of 0
+ * means the workgroup (or wave) had no work there.  *words_written gets the
+ * word count and *clock_khz the clock rate.  Errors: MK_E_INVAL (null,
+ * capacity too small, handle loaded without cfg.trace), MK_E_HIP. */
 int mk_trace_copy(mk_handle* h, uint64_t* out, int64_t capacity_words, int64_t* words_written,
                   int32_t* clock_khz);
 

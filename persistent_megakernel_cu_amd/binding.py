@@ -27,6 +27,8 @@ MK_E_NOMEM = -7
 MK_E_UNSUPPORTED = -8
 MK_E_DEVICE = -9
 
+TRACE_STAMPS = 20  # stamps per (workgroup, stage) trace record
+
 MODE_MEGA = 0
 MODE_MULTI = 1
 MODE_GRAPH = 2
@@ -195,14 +197,14 @@ class Engine:
         rc = lib().mk_plan_describe(ctypes.byref(self.cfg), self.cfg.num_wgs or 256, ctypes.byref(info))
         if rc != MK_OK:
             raise MkError(rc, "mk_plan_describe")
-        cap = 4 * 4096 * info.num_stages
+        cap = TRACE_STAMPS * 4096 * info.num_stages
         buf = np.zeros(cap, dtype=np.uint64)
         n = ctypes.c_int64()
         khz = ctypes.c_int32()
         rc = lib().mk_trace_copy(self._h, buf.ctypes.data, cap, ctypes.byref(n), ctypes.byref(khz))
         if rc != MK_OK:
             raise MkError(rc, "mk_trace_copy")
-        return buf[: n.value].reshape(-1, info.num_stages, 4), khz.value
+        return buf[: n.value].reshape(-1, info.num_stages, TRACE_STAMPS), khz.value
 
     def status(self) -> MkStatus:
         s = MkStatus()

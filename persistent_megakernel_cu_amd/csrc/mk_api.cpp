@@ -352,7 +352,7 @@ int mk_load(const mk_config* cfg, const mk_weights* w, mk_handle** out) {
 
   HIP_OR(hipStreamCreateWithFlags(&h->capture_stream, hipStreamNonBlocking));
   if (cfg->trace) {
-    const size_t tb = (size_t)p.W * p.stages * 4 * sizeof(uint64_t);
+    const size_t tb = (size_t)p.W * p.stages * mk::kTraceStamps * sizeof(uint64_t);
     HIP_OR(hipMalloc(&h->trace, tb));
     HIP_OR(hipMemset(h->trace, 0, tb));
   }
@@ -445,7 +445,7 @@ void mk_free(mk_handle* h) {
 
 int mk_trace_copy(mk_handle* h, uint64_t* out, int64_t capacity_words, int64_t* words_written, int32_t* clock_khz) {
   if (!h || !out || !h->trace) return MK_E_INVAL;
-  const int64_t n = (int64_t)h->plan.W * h->plan.stages * 4;
+  const int64_t n = (int64_t)h->plan.W * h->plan.stages * mk::kTraceStamps;
   if (capacity_words < n) return MK_E_INVAL;
   if (hipDeviceSynchronize() != hipSuccess) {
     (void)hipGetLastError();

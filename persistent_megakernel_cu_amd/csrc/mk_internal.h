@@ -19,8 +19,9 @@ constexpr int kUnitBytes = 1024;
 constexpr int kUnitElems = kUnitBytes / 2;  // bf16 elements per unit
 // Rows are padded to a multiple of one unit.
 constexpr int kRowAlign = kUnitElems;
-// Per-wave LDS ring of weight units kept in flight (12 KiB per wave).
-constexpr int kRing = 12;
+// Per-wave LDS ring of weight units kept in flight (8 KiB per wave, 64 KiB
+// per workgroup).  A compile-time depth keeps every wait count an immediate.
+constexpr int kRing = 8;
 // Largest group of query heads sharing one KV head.
 constexpr int kMaxGroup = 8;
 // Largest number of split items (pairs << kslog) of one task (LDS partials).
@@ -126,7 +127,7 @@ struct Params {
   int32_t res_floats;
 
   uint64_t watchdog_ticks;  // wall-clock ticks (100 MHz on MI355X)
-  uint64_t* trace;          // [num_wgs][num_stages][4] stamps, or null
+  uint64_t* trace;          // [num_wgs][num_stages][kTraceStamps] stamps, or null
 
   // per step
   const int32_t* token;  // [B]
@@ -138,6 +139,11 @@ struct Params {
   uint32_t epoch;
   const StepArgs* dargs; // non-null: read pos and epoch from here (graph mode)
 };
+
+// Trace record of one (workgroup, stage): entered, inputs ready, compute done,
+// left, then for each of the kWaves waves the time it finished its own work,
+// then for each wave the time its first weight unit of the task was in hand.
+constexpr int kTraceStamps = 4 + 2 * kWaves;
 
 // LDS bytes of the per-wave rings.
 constexpr int kRingBytes = kWaves * kRing * kUnitBytes;

@@ -69,6 +69,20 @@ __device__ __forceinline__ uint4 ring_read(uint32_t lds_addr) {
 
 __device__ __forceinline__ void wait_all_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Wait until at most N vector-memory loads of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
+// Four LDS reads of 16 bytes issued back to back, one wait for all of them.
+__device__ __forceinline__ void lds_read4(uint4 (&v)[4], const uint32_t (&a)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+      : "memory");
+}
+
 __device__ __forceinline__ void st_tag(uint64_t* p, float v, uint32_t tag) {
   __hip_atomic_store(p, ((uint64_t)tag << 32) | (uint64_t)__float_as_uint(v), __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);
@@ -139,6 +153,19 @@ __device__ __forceinline__ float dot8(const uint4 w, const float* x) {
   return s;
 }
 
+// Same with the 8 activations already in registers.
+__device__ __forceinline__ float dot8r(const uint4 w, const float4 a, const float4 b) {
+  float s = bf_lo(w.x) * a.x;
+  s = fmaf(bf_hi(w.x), a.y, s);
+  s = fmaf(bf_lo(w.y), a.z, s);
+  s = fmaf(bf_hi(w.y), a.w, s);
+  s = fmaf(bf_lo(w.z), b.x, s);
+  s = fmaf(bf_hi(w.z), b.y, s);
+  s = fmaf(bf_lo(w.w), b.z, s);
+  s = fmaf(bf_hi(w.w), b.w, s);
+  return s;
+}
+
 // Argmax key: larger key = larger value, ties -> lower index; 0 = no candidate.
 __device__ __forceinline__ uint64_t amax_key(float v, int idx) {
   if (idx < 0) return 0;
@@ -170,6 +197,15 @@ struct Ctx {
 // Trace stamp k of the current (workgroup, stage) record.
 __device__ __forceinline__ void mark(Ctx& c, int k) {
   if (c.tr != nullptr && c.tid == 0) c.tr[k] = wall_clock64();
+}
+// Per-wave stamp: this wave finished its own part of the task.
+__device__ __forceinline__ void mark_wave(Ctx& c) {
+  if (c.tr != nullptr && c.lane == 0) c.tr[4 + c.wave] = wall_clock64();
+}
+// Per-wave stamp: this wave's first weight unit of the task is in registers.
+__device__ __forceinline__ void mark_first(Ctx& c, bool& done) {
+  if (!done && c.tr != nullptr && c.lane == 0) c.tr[4 + kWaves + c.wave] = wall_clock64();
+  done = true;
 }
 
 // Latch the first device error; a timeout also stops every workgroup.
@@ -237,17 +273,17 @@ __device__ __forceinline__ void seg_store(const Seg (&seg)[NSEG], int i, uint64_
   }
 }
 
-template <int NSEG>
+template <int NSEG, int NL = kStageLoads>
 __device__ __forceinline__ bool stage_tagged(const Params& P, Ctx& c, const Seg (&seg)[NSEG], int stage,
                                              float* zdst = nullptr, int zfrom = 0, int zto = 0) {
   int total = 0;
 #pragma unroll
   for (int k = 0; k < NSEG; ++k) total += seg[k].n;
   bool stop = false;
-  for (int i0 = 0; i0 == 0 || i0 < total; i0 += kThreads * kStageLoads) {
-    uint64_t w[kStageLoads];
+  for (int i0 = 0; i0 == 0 || i0 < total; i0 += kThreads * NL) {
+    uint64_t w[NL];
 #pragma unroll
-    for (int j = 0; j < kStageLoads; ++j) {
+    for (int j = 0; j < NL; ++j) {
       const uint64_t* p = seg_src(seg, i0 + j * kThreads + c.tid);
       w[j] = p ? ld_tag(p) : ((uint64_t)c.epoch << 32);
     }
@@ -255,14 +291,14 @@ __device__ __forceinline__ bool stage_tagged(const Params& P, Ctx& c, const Seg 
     while (!stop) {
       bool ready = true;
 #pragma unroll
-      for (int j = 0; j < kStageLoads; ++j) ready &= (uint32_t)(w[j] >> 32) == c.epoch;
+      for (int j = 0; j < NL; ++j) ready &= (uint32_t)(w[j] >> 32) == c.epoch;
       if (ready) break;
       if (poll_stop(P, t0, stage, (uint32_t)(w[0] >> 32))) {
         stop = true;
         break;
       }
 #pragma unroll
-      for (int j = 0; j < kStageLoads; ++j) {
+      for (int j = 0; j < NL; ++j) {
         if ((uint32_t)(w[j] >> 32) != c.epoch) {
           const uint64_t* p = seg_src(seg, i0 + j * kThreads + c.tid);
           if (p) w[j] = ld_tag(p);
@@ -274,7 +310,7 @@ __device__ __forceinline__ bool stage_tagged(const Params& P, Ctx& c, const Seg 
       for (int i = zfrom + c.tid; i < zto; i += kThreads) zdst[i] = 0.f;
     }
 #pragma unroll
-    for (int j = 0; j < kStageLoads; ++j) seg_store(seg, i0 + j * kThreads + c.tid, w[j]);
+    for (int j = 0; j < NL; ++j) seg_store(seg, i0 + j * kThreads + c.tid, w[j]);
   }
   if (stop) c.flags[0] = 1;
   __syncthreads();
@@ -455,18 +491,57 @@ __device__ __forceinline__ void loader_issue(const Params& P, Stream& st, int b,
   }
 }
 
-// Next unit of this wave's stream; refills the freed slot.
+// Issue loads into free ring slots, at most `max` of them.
+__device__ __forceinline__ void top_up(const Params& P, Stream& st, int b, int wave, int lane, int max) {
+  while (max-- > 0 && !st.ldone && st.issued - st.consumed < kRing) loader_issue(P, st, b, wave, lane);
+}
+
+// Next unit of this wave's stream; the freed slot is refilled with the next
+// unit of the stream, whatever its stage, so the ring stays full and the
+// wait count is a constant (loads complete in issue order; once the stream
+// has no units left the ring drains and the wait is for everything).
 __device__ __forceinline__ uint4 consume_unit(const Params& P, Stream& st, int b, int wave, int lane) {
   const uint32_t a = st.ring + (uint32_t)st.cslot * kUnitBytes + (uint32_t)lane * 16u;
-  uint4 v;
-  if (st.issued - st.consumed == kRing)
-    v = ring_read<kRing - 1>(a);
-  else
-    v = ring_read<0>(a);
+  const uint4 v = (st.issued - st.consumed == kRing) ? ring_read<kRing - 1>(a) : ring_read<0>(a);
   ++st.consumed;
   st.cslot = (st.cslot + 1 == kRing) ? 0 : st.cslot + 1;
-  loader_issue(P, st, b, wave, lane);
+  top_up(P, st, b, wave, lane, 1);
   return v;
+}
+
+// Next four units of this wave's stream: one vmcnt wait for the fourth, one
+// LDS wait for all four reads, then four refills.
+__device__ __forceinline__ void take4(const Params& P, Stream& st, int b, int wave, int lane, uint4 (&v)[4]) {
+  if (st.issued - st.consumed == kRing)
+    wait_vm<kRing - 4>();
+  else
+    wait_vm<0>();
+  uint32_t a[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    int sl = st.cslot + k;
+    sl = sl >= kRing ? sl - kRing : sl;
+    a[k] = st.ring + (uint32_t)sl * kUnitBytes + (uint32_t)lane * 16u;
+  }
+  lds_read4(v, a);
+  st.consumed += 4;
+  st.cslot = st.cslot + 4 >= kRing ? st.cslot + 4 - kRing : st.cslot + 4;
+  top_up(P, st, b, wave, lane, 4);
+}
+
+// Dot product of `n` consecutive units of the stream with act[col*512 ...]:
+// batches of four, then single units.
+__device__ __forceinline__ float dot_units(const Params& P, Stream& st, Ctx& c, const float* xa, int col, int n) {
+  float a = 0.f;
+  int j = 0;
+  for (; j + 4 <= n; j += 4) {
+    uint4 v[4];
+    take4(P, st, c.b, c.wave, c.lane, v);
+    const float* x = xa + (col + j) * kUnitElems;
+    a += (dot8(v[0], x) + dot8(v[1], x + kUnitElems)) + (dot8(v[2], x + 2 * kUnitElems) + dot8(v[3], x + 3 * kUnitElems));
+  }
+  for (; j < n; ++j) a += dot8(consume_unit(P, st, c.b, c.wave, c.lane), xa + (col + j) * kUnitElems);
+  return a;
 }
 
 // ---------------------------------------------------------------------------
@@ -499,24 +574,38 @@ __device__ __forceinline__ bool gemv_prologue(const Params& P, Ctx& c, const Tas
     const int np = OP == OP_OPROJ ? P.QDp : P.Fp;
     const uint64_t* src = OP == OP_OPROJ ? P.o + (size_t)l * P.QD : P.h + (size_t)l * P.F;
     const int r0 = 2 * (int)t.a0, nr = 2 * (int)(t.a1 - t.a0);
-    if (OP == OP_OPROJ && l == 0) {
-      const Seg seg[1] = {{c.act, src, n, 1.f}};
-      if (!stage_tagged(P, c, seg, s, c.act, n, np)) return false;
-      // the residual of layer 0 is the embedding row itself
-      if (c.tid == 0) {
+    // The residual rows were produced at least two stages earlier: read them
+    // into registers before waiting for the activation (nr <= 512 rows).
+    const uint64_t* rs = OP == OP_OPROJ ? (l == 0 ? nullptr : x_in(P, l) + r0) : P.x_attn + (size_t)l * P.H + r0;
+    uint64_t rw = (uint64_t)c.epoch << 32;
+    if (c.tid < nr) {
+      if (rs) {
+        rw = ld_tag(rs + c.tid);
+      } else {  // layer 0: the residual is the embedding row itself
         int tok = P.token[0];
-        if (tok < 0 || tok >= P.V) tok = 0;
-        c.flags[2] = tok;
+        tok = (tok < 0 || tok >= P.V) ? 0 : tok;
+        rw |= (uint64_t)((uint32_t)P.embed[(size_t)tok * P.H + r0 + c.tid] << 16);
       }
-      __syncthreads();
-      const uint16_t* row = P.embed + (size_t)c.flags[2] * P.H + r0;
-      for (int i = c.tid; i < nr; i += kThreads) c.res[i] = bf16_to_f32(row[i]);
-      __syncthreads();
+    }
+    const Seg seg[1] = {{c.act, src, n, 1.f}};
+    if (OP == OP_DOWN) {
+      if (!stage_tagged<1, 2 * kStageLoads>(P, c, seg, s, c.act, n, np)) return false;
     } else {
-      const uint64_t* rs = OP == OP_OPROJ ? x_in(P, l) + r0 : P.x_attn + (size_t)l * P.H + r0;
-      const Seg seg[2] = {{c.act, src, n, 1.f}, {c.res, rs, nr, 1.f}};
       if (!stage_tagged(P, c, seg, s, c.act, n, np)) return false;
     }
+    if (c.tid < nr) {
+      uint64_t t0 = 0;
+      while ((uint32_t)(rw >> 32) != c.epoch) {
+        if (poll_stop(P, t0, s, (uint32_t)(rw >> 32))) {
+          c.flags[0] = 1;
+          break;
+        }
+        rw = ld_tag(rs + c.tid);
+      }
+      c.res[c.tid] = __uint_as_float((uint32_t)rw);
+    }
+    __syncthreads();
+    if (c.flags[0]) return false;
   }
   return true;
 }
@@ -630,14 +719,38 @@ __device__ __forceinline__ bool gemv_task(const Params& P, Ctx& c, Stream& st, c
   if (t.kslog == 0) {
     // whole pairs per wave; the wave finishes each pair
     const int half = (int)t.nu >> 1;  // units per row
-    for (uint32_t pair = t.a0 + (uint32_t)c.wave; pair < t.a1; pair += kWaves) {
-      float a0 = 0.f, a1 = 0.f;
-      for (int j = 0; j < half; ++j) a0 += dot8(consume_unit(P, st, c.b, c.wave, c.lane), xa + j * kUnitElems);
-      for (int j = 0; j < half; ++j) a1 += dot8(consume_unit(P, st, c.b, c.wave, c.lane), xa + j * kUnitElems);
-      a0 = wave_sum(a0);
-      a1 = wave_sum(a1);
-      gemv_epilogue<OP>(P, c, t, pair, a0, a1, best, c.lane == 0, c.lane == 1);
+    if (half == 4) {
+      // rows of 2048: this lane's activation slice stays in registers for the task
+      float4 xr[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        xr[2 * j] = *reinterpret_cast<const float4*>(xa + j * kUnitElems);
+        xr[2 * j + 1] = *reinterpret_cast<const float4*>(xa + j * kUnitElems + 4);
+      }
+      bool first = false;
+      for (uint32_t pair = t.a0 + (uint32_t)c.wave; pair < t.a1; pair += kWaves) {
+        uint4 v[4];
+        take4(P, st, c.b, c.wave, c.lane, v);
+        mark_first(c, first);
+        float a0 = (dot8r(v[0], xr[0], xr[1]) + dot8r(v[1], xr[2], xr[3])) +
+                   (dot8r(v[2], xr[4], xr[5]) + dot8r(v[3], xr[6], xr[7]));
+        take4(P, st, c.b, c.wave, c.lane, v);
+        float a1 = (dot8r(v[0], xr[0], xr[1]) + dot8r(v[1], xr[2], xr[3])) +
+                   (dot8r(v[2], xr[4], xr[5]) + dot8r(v[3], xr[6], xr[7]));
+        a0 = wave_sum(a0);
+        a1 = wave_sum(a1);
+        gemv_epilogue<OP>(P, c, t, pair, a0, a1, best, c.lane == 0, c.lane == 1);
+      }
+    } else {
+      for (uint32_t pair = t.a0 + (uint32_t)c.wave; pair < t.a1; pair += kWaves) {
+        float a0 = dot_units(P, st, c, xa, 0, half);
+        float a1 = dot_units(P, st, c, xa, 0, half);
+        a0 = wave_sum(a0);
+        a1 = wave_sum(a1);
+        gemv_epilogue<OP>(P, c, t, pair, a0, a1, best, c.lane == 0, c.lane == 1);
+      }
     }
+    mark_wave(c);
   } else {
     // split items: row segments spread over all waves, partials added in LDS
     const uint32_t ks = 1u << t.kslog, hks = ks >> 1;
@@ -645,11 +758,15 @@ __device__ __forceinline__ bool gemv_task(const Params& P, Ctx& c, Stream& st, c
     const uint32_t n_items = (t.a1 - t.a0) << t.kslog;
     for (uint32_t i = (uint32_t)c.wave; i < n_items; i += kWaves) {
       const int col = (int)(i & (hks - 1u)) * upi;  // first unit of the item inside its row
-      float a = 0.f;
-      for (int j = 0; j < upi; ++j) a += dot8(consume_unit(P, st, c.b, c.wave, c.lane), xa + (col + j) * kUnitElems);
-      a = wave_sum(a);
+      if (i == (uint32_t)c.wave && c.tr != nullptr) {
+        wait_vm<0>();
+        bool f = false;
+        mark_first(c, f);
+      }
+      float a = wave_sum(dot_units(P, st, c, xa, col, upi));
       if (c.lane == 0) c.part[i] = a;
     }
+    mark_wave(c);
     __syncthreads();
     for (uint32_t pl = (uint32_t)c.tid; pl < t.a1 - t.a0; pl += kThreads) {
       float v0 = 0.f, v1 = 0.f;
@@ -827,6 +944,7 @@ __device__ __forceinline__ bool attn_task(const Params& P, Ctx& c, const Task& t
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int e = 0; e < DPL; ++e) wpart[(c.wave * G + h) * D + c.lane * DPL + e] = acc[h][e];
+  mark_wave(c);
   __syncthreads();
   mark(c, 2);
 
@@ -909,16 +1027,17 @@ __device__ __forceinline__ void run_stages(const Params& P, int s_begin, int s_e
   __syncthreads();
 
   Stream st;
-  st.ring = lds_byte(smem) + (uint32_t)c.wave * (kRing * kUnitBytes);
+  st.ring = lds_byte(smem) + (uint32_t)c.wave * (uint32_t)(kRing * kUnitBytes);
   st.issued = st.consumed = st.lslot = st.cslot = 0;
   st.s_end = s_end;
   st.ldone = false;
   loader_seek(P, st, s_begin, c.b, c.wave);
-  for (int i = 0; i < kRing; ++i) loader_issue(P, st, c.b, c.wave, c.lane);
+  top_up(P, st, c.b, c.wave, c.lane, kRing);
 
   for (int s = s_begin; s < s_end; ++s) {
     const Task t = task_at(P, s, c.b);
-    c.tr = (P.trace != nullptr && t.op != OP_NONE) ? P.trace + ((size_t)c.b * P.num_stages + s) * 4 : nullptr;
+    c.tr = (P.trace != nullptr && t.op != OP_NONE) ? P.trace + ((size_t)c.b * P.num_stages + s) * kTraceStamps
+                                                   : nullptr;
     mark(c, 0);
     bool ok = true;
     switch (t.op) {

@@ -166,6 +166,8 @@ int plan_build(const mk_config& c, int W, Plan& p) {
   const int attn_floats = p.G * p.D + 2 * p.D + kMaxChunk * p.G + kWaves * p.G * p.D + 2 * kMaxGroup;
   p.act_floats = round_up(std::max(std::max(p.Hp, p.QDp), std::max(p.Fp, attn_floats)), 4);
   p.res_floats = round_up(std::max(max_res_rows, 4), 4);
+  if (max_res_rows > kThreads) return fail(p, MK_E_UNSUPPORTED, "more than 512 residual rows per workgroup");
+  p.ring_units = kRing;
   p.lds_act = kRingBytes;
   p.lds_res = p.lds_act + p.act_floats * 4;
   p.lds_rope = p.lds_res + p.res_floats * 4;
