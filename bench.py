@@ -27,6 +27,36 @@ sys.path.insert(0, ROOT)
 METRIC = "µs/token batch-1 decode (Llama-1B shape) + achieved HBM GB/s vs 8 TB/s peak"
 HBM_PEAK_GBPS = 8000.0
 
+# HBM bytes per decode step of the megakernel at the llama1b workload, from
+# rocprofv3 FETCH_SIZE / WRITE_SIZE scaled by a 1 GiB copy (the summary and
+# commands are in profiles/mk_persistent_llama1b_hbm_bytes.md).  They describe
+# the kernel sources whose hash is recorded; any other source gives null.
+MEASURED_TRAFFIC = {
+    "sources_sha256_prefix": "379c62f498e3f366",
+    "fetch_bytes": 2.5096e9,
+    "write_bytes": 7.05e6,
+    "fetch_factor": 2.000,
+    "write_factor": 1.000,
+}
+KERNEL_SOURCES = ("csrc/mk_kernels.hip", "csrc/mk_internal.h", "csrc/mk_plan.cpp")
+
+
+def kernel_sources_hash() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "persistent_megakernel_cu_amd", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed counters, or None when the kernel changed since."""
+    if workload != "llama1b" or kernel_sources_hash() != MEASURED_TRAFFIC["sources_sha256_prefix"]:
+        return None
+    return MEASURED_TRAFFIC["fetch_bytes"] + MEASURED_TRAFFIC["write_bytes"]
+
 
 def algorithmic_bytes(shape, pos: int, batch: int = 1) -> int:
     """Bytes one decode step must move: every weight once, the norm gains, the
@@ -220,8 +250,9 @@ def main() -> int:
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(args.workload),
             "bytes_per_step": int(avg_bytes),
+            "traffic_unit": "HBM bytes per launch (one launch = one decode step)",
         },
         "baselines": {m: {"us_per_token": round(v * 1e3, 2), "tokens_per_s": round(1e3 / v, 1)}
                       for m, v in results.items()},
