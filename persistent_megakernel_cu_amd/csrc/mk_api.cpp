@@ -150,6 +150,7 @@ Params make_params(mk_handle* h) {
   P.lds_rope = p.lds_rope;
   P.lds_misc = p.lds_misc;
   P.lds_part = p.lds_part;
+  P.lds_tape = p.lds_tape;
   P.act_floats = p.act_floats;
   P.res_floats = p.res_floats;
   P.watchdog_ticks = h->watchdog_ticks;

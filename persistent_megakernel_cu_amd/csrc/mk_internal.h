@@ -123,6 +123,7 @@ struct Params {
   int32_t lds_rope;      // cos/sin of this position
   int32_t lds_misc;      // reductions and flags
   int32_t lds_part;      // [kMaxItems] partial sums of split items
+  int32_t lds_tape;      // this workgroup's task records, one per stage
   int32_t act_floats;
   int32_t res_floats;
 

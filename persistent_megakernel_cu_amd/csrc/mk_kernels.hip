@@ -421,23 +421,28 @@ __device__ __forceinline__ bool stage_normed(const Params& P, Ctx& c, float* dst
 // the per-wave weight stream (LDS ring, loader running ahead of the consumer)
 // ---------------------------------------------------------------------------
 
-// Task records are immutable during a launch; read them with a scalar load so
-// that neither the loader nor the consumer waits on vector-memory counters.
-__device__ __forceinline__ Task task_at(const Params& P, int s, int b) {
-  typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
-  const Task* ptr = P.tape + (size_t)s * P.num_wgs + b;
-  u32x8 r;
-  asm volatile("s_load_dwordx8 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(r) : "s"(ptr));
+// Task record of stage s for this workgroup, from the copy of its tape column
+// that the workgroup keeps in LDS (a record read from memory by a scalar load
+// can miss in the scalar cache for a microsecond, and the LDS reads of the
+// weight ring would wait on that same counter).
+__device__ __forceinline__ Task task_at(uint32_t tape_lds, int idx) {
+  uint4 lo, hi;
+  const uint32_t a = tape_lds + (uint32_t)idx * (uint32_t)sizeof(Task);
+  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:16\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(lo), "=&v"(hi)
+               : "v"(a)
+               : "memory");
+  const uint32_t r0 = __builtin_amdgcn_readfirstlane(lo.x);
   Task t;
-  t.op = (uint8_t)(r[0] & 0xffu);
-  t.region = (uint8_t)((r[0] >> 8) & 0xffu);
-  t.layer = (uint16_t)(r[0] >> 16);
-  t.a0 = r[1];
-  t.a1 = r[2];
-  t.nu = r[3];
-  t.wofs = (uint64_t)r[4] | ((uint64_t)r[5] << 32);
-  t.ntasks = r[6];
-  t.kslog = r[7];
+  t.op = (uint8_t)(r0 & 0xffu);
+  t.region = (uint8_t)((r0 >> 8) & 0xffu);
+  t.layer = (uint16_t)(r0 >> 16);
+  t.a0 = __builtin_amdgcn_readfirstlane(lo.y);
+  t.a1 = __builtin_amdgcn_readfirstlane(lo.z);
+  t.nu = __builtin_amdgcn_readfirstlane(lo.w);
+  t.wofs = (uint64_t)__builtin_amdgcn_readfirstlane(hi.x) | ((uint64_t)__builtin_amdgcn_readfirstlane(hi.y) << 32);
+  t.ntasks = __builtin_amdgcn_readfirstlane(hi.z);
+  t.kslog = __builtin_amdgcn_readfirstlane(hi.w);
   return t;
 }
 
@@ -446,8 +451,9 @@ __device__ __forceinline__ Task task_at(const Params& P, int s, int b) {
 // [(i & (2^kslog - 1)) * upi, + upi) of that pair, upi = nu >> kslog.
 struct Stream {
   uint32_t ring;  // LDS byte address of this wave's ring
+  uint32_t tape;  // LDS byte address of the task record of stage s_begin
   int issued, consumed, lslot, cslot;
-  int ls, s_end;
+  int ls, s_begin, s_end;
   uint32_t litem, lnitems, lkslog, lupi, lu, la0, lnu;
   const char* lbase;
   bool ldone;
@@ -455,7 +461,7 @@ struct Stream {
 
 __device__ __forceinline__ void loader_seek(const Params& P, Stream& st, int s, int b, int wave) {
   for (; s < st.s_end; ++s) {
-    const Task t = task_at(P, s, b);
+    const Task t = task_at(st.tape, s - st.s_begin);
     if (op_is_gemv(t.op)) {
       const uint32_t n_items = (t.a1 - t.a0) << t.kslog;
       if ((uint32_t)wave < n_items) {
@@ -1024,18 +1030,29 @@ __device__ __forceinline__ void run_stages(const Params& P, int s_begin, int s_e
   c.part = reinterpret_cast<float*>(smem + P.lds_part);
   if (c.tid < 4) c.flags[c.tid] = 0;
   c.tr = nullptr;
+  // this workgroup's column of the tape, stages [s_begin, s_end), into LDS
+  {
+    constexpr int kWords = (int)(sizeof(Task) / 4);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(smem + P.lds_tape);
+    for (int i = c.tid; i < (s_end - s_begin) * kWords; i += kThreads) {
+      const int s = s_begin + i / kWords;
+      dst[i] = reinterpret_cast<const uint32_t*>(P.tape + (size_t)s * P.num_wgs + c.b)[i % kWords];
+    }
+  }
   __syncthreads();
 
   Stream st;
   st.ring = lds_byte(smem) + (uint32_t)c.wave * (uint32_t)(kRing * kUnitBytes);
+  st.tape = lds_byte(smem) + (uint32_t)P.lds_tape;
   st.issued = st.consumed = st.lslot = st.cslot = 0;
+  st.s_begin = s_begin;
   st.s_end = s_end;
   st.ldone = false;
   loader_seek(P, st, s_begin, c.b, c.wave);
   top_up(P, st, c.b, c.wave, c.lane, kRing);
 
   for (int s = s_begin; s < s_end; ++s) {
-    const Task t = task_at(P, s, c.b);
+    const Task t = task_at(st.tape, s - s_begin);
     c.tr = (P.trace != nullptr && t.op != OP_NONE) ? P.trace + ((size_t)c.b * P.num_stages + s) * kTraceStamps
                                                    : nullptr;
     mark(c, 0);

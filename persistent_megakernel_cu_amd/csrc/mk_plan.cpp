@@ -173,7 +173,8 @@ int plan_build(const mk_config& c, int W, Plan& p) {
   p.lds_rope = p.lds_res + p.res_floats * 4;
   p.lds_misc = p.lds_rope + round_up(p.D, 4) * 4;
   p.lds_part = p.lds_misc + 256;
-  p.lds_bytes = p.lds_part + kMaxItems * 4;
+  p.lds_tape = p.lds_part + kMaxItems * 4;
+  p.lds_bytes = p.lds_tape + p.stages * (int)sizeof(Task);
   if (p.lds_bytes > 160 * 1024) return fail(p, MK_E_UNSUPPORTED, "LDS plan exceeds 160 KiB per workgroup");
   return MK_OK;
 }

@@ -33,7 +33,7 @@ struct Plan {
 
   // LDS layout
   int act_floats = 0, res_floats = 0, ring_units = 0;
-  int lds_act = 0, lds_res = 0, lds_rope = 0, lds_misc = 0, lds_part = 0, lds_bytes = 0;
+  int lds_act = 0, lds_res = 0, lds_rope = 0, lds_misc = 0, lds_part = 0, lds_tape = 0, lds_bytes = 0;
 
   std::string error;
 };
