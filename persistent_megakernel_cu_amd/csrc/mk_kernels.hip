@@ -790,60 +790,69 @@ __device__ __forceinline__ bool gemv_task(const Params& P, Ctx& c, Stream& st, c
 // attention: one (kv head, chunk) per task, G query heads of D dims
 // ---------------------------------------------------------------------------
 
-// Scores: thread i < len owns position t0 + i and dots the whole K row with
-// the G queries (no cross-lane sum).  P.V: wave w owns positions t0 + w + 8j
-// and lane l owns dims [l * D/64, (l+1) * D/64); the eight waves' partial sums
-// are added in LDS in wave order.  The K row of each score thread and the V
-// values of each P.V lane are read before the task waits for this step's q, k
-// and v: every slot below pos was written by an earlier step.
+// Layout: thread tid owns dims [8 * (tid % NT), +8) (one 16-byte slice of a
+// K or V row, NT = D / 8 threads per row) of positions t0 + j * PPP + tid / NT
+// for passes j < NPASS, PPP = 512 / NT positions per pass.  K and V of every
+// owned position sit in registers (read before the task waits for this
+// step's q, k and v: every slot below pos was written by an earlier step), q
+// slices too, so scores and P.V need no LDS traffic.  A score is the sum of
+// the NT slice dots (DPP within a row); each wave keeps its own softmax
+// maximum and sum over its positions; the eight waves' {max, sum, P.V} are
+// merged once, in wave order, after the only barrier.
+template <int NT>
+__device__ __forceinline__ float slice_sum(float a) {
+  a += dpp<0xB1>(a);
+  a += dpp<0x4E>(a);
+  a += dpp<0x141>(a);
+  if (NT == 16) a += dpp<0x140>(a);
+  return a;
+}
+
+// Sum over the position groups of a wave (lanes with equal lane % NT).
+template <int NT>
+__device__ __forceinline__ float group_sum(float a) {
+  if (NT == 8) a += dpp<0x128>(a);  // row_ror:8 == lane ^ 8 inside a row of 16
+  a += __shfl_xor(a, 16);
+  a += __shfl_xor(a, 32);
+  return a;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+}
+
 template <int G, int D>
 __device__ __forceinline__ bool attn_task(const Params& P, Ctx& c, const Task& t, int s) {
-  constexpr int NV = kMaxChunk / kWaves;  // P.V positions per wave
-  constexpr int DPL = D / 64;             // P.V dims per lane
+  constexpr int NT = D / 8;                 // threads per K/V row
+  constexpr int PPP = kThreads / NT;        // positions per pass
+  constexpr int NPASS = kMaxChunk / PPP;    // passes over a full chunk
   const int l = t.layer, g = (int)t.a0, ch = (int)t.a1;
   const int C = P.attn_chunks;
   const int n = c.pos + 1;
   const int len0 = (n + C - 1) / C;
   const int t0 = min(n, ch * len0), t1 = min(n, t0 + len0);
-  const int len = t1 - t0;
 
   const size_t head_off = ((size_t)l * P.NKV + g) * P.S * D;
-  const uint16_t* kc = P.kcache + head_off;
-  const uint16_t* vc = P.vcache + head_off;
-  // TPP threads per score position, each over 64 of the D dims
-  constexpr int TPP = D / 64;
-  const int sp = c.tid / TPP;            // position slot of this thread
-  const int dq = (c.tid % TPP) * 64;     // first dim of this thread
-  const int ts = t0 + sp;
-  const bool scorer = sp < len;
-  // Branch-free prefetch: every lane loads from an in-bounds slot (slot 0 when
-  // its own slot is out of range or is pos) and the raw bits are masked at
-  // use, so all loads issue back to back instead of one wait per load.
-  uint4 kr[8];
-  {
-    const int tk = (scorer && ts != c.pos) ? ts : 0;
-    const uint4* row = reinterpret_cast<const uint4*>(kc + (size_t)tk * D + dq);
+  const int ds = c.tid % NT;               // dim slice
+  const int pg = c.tid / NT;               // position group
+  // Branch-free prefetch: a position out of range, or pos itself, reads slot
+  // 0 (in bounds) and is replaced or masked after the wait.
+  uint4 kr[NPASS], vr[NPASS];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) kr[q] = row[q];
-  }
-  uint32_t vv[NV];
-#pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const int tv = t0 + c.wave + kWaves * j;
-    const int tl = (tv < t1 && tv != c.pos) ? tv : 0;
-    if (DPL == 1)
-      vv[j] = vc[(size_t)tl * D + c.lane];
-    else
-      vv[j] = reinterpret_cast<const uint32_t*>(vc + (size_t)tl * D)[c.lane];
+  for (int j = 0; j < NPASS; ++j) {
+    const int tp = t0 + j * PPP + pg;
+    const int tl = (tp < t1 && tp != c.pos) ? tp : 0;
+    const size_t o = head_off + (size_t)tl * D + ds * 8;
+    kr[j] = *reinterpret_cast<const uint4*>(P.kcache + o);
+    vr[j] = *reinterpret_cast<const uint4*>(P.vcache + o);
   }
 
-  float* qs = c.act;                    // [G][D], pre-scaled by 1/sqrt(D)
-  float* kcur = qs + G * D;             // [D]
-  float* vcur = kcur + D;               // [D]
-  float* sc = vcur + D;                 // [kMaxChunk][G] scores, then probabilities
-  float* wpart = sc + kMaxChunk * G;    // [kWaves][G][D]
-  float* wm = wpart + kWaves * G * D;   // [kMaxGroup] per-head max
-  float* wl = wm + kMaxGroup;           // [kMaxGroup] per-head sum
+  float* qs = c.act;                       // [G][D], pre-scaled by 1/sqrt(D)
+  float* kcur = qs + G * D;                // [D]
+  float* vcur = kcur + D;                  // [D]
+  float* wpart = vcur + D;                 // [kWaves][G][D]
+  float* wm = wpart + kWaves * G * D;      // [kWaves][G] per-wave max
+  float* wl = wm + kWaves * G;             // [kWaves][G] per-wave sum
   {
     const Seg seg[3] = {{qs, P.q + (size_t)l * P.QD + (size_t)g * G * D, G * D, P.qscale},
                         {kcur, P.kvcur + (size_t)l * 2 * P.KVD + (size_t)g * D, D, 1.f},
@@ -852,128 +861,113 @@ __device__ __forceinline__ bool attn_task(const Params& P, Ctx& c, const Task& t
   }
   mark(c, 1);
 
-  // The row at pos came from this step's staged k and v; their values are
-  // bf16-exact, so they go back into the prefetch registers as bf16 bits and
-  // the loops below need no per-position branch.
-  if (scorer && ts == c.pos) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const float* k = kcur + dq + q * 8;
-      kr[q].x = (__float_as_uint(k[0]) >> 16) | (__float_as_uint(k[1]) & 0xffff0000u);
-      kr[q].y = (__float_as_uint(k[2]) >> 16) | (__float_as_uint(k[3]) & 0xffff0000u);
-      kr[q].z = (__float_as_uint(k[4]) >> 16) | (__float_as_uint(k[5]) & 0xffff0000u);
-      kr[q].w = (__float_as_uint(k[6]) >> 16) | (__float_as_uint(k[7]) & 0xffff0000u);
-    }
-  }
+  // this step's row (bf16-exact values) goes back into the registers as bits
   {
-    const uint32_t vcb = DPL == 1 ? (__float_as_uint(vcur[c.lane]) >> 16)
-                                  : ((__float_as_uint(vcur[2 * c.lane]) >> 16) |
-                                     (__float_as_uint(vcur[2 * c.lane + 1]) & 0xffff0000u));
+    const float4 k0 = *reinterpret_cast<const float4*>(kcur + ds * 8);
+    const float4 k1 = *reinterpret_cast<const float4*>(kcur + ds * 8 + 4);
+    const float4 v0 = *reinterpret_cast<const float4*>(vcur + ds * 8);
+    const float4 v1 = *reinterpret_cast<const float4*>(vcur + ds * 8 + 4);
+    const uint4 kb = {pack_bf16x2(k0.x, k0.y), pack_bf16x2(k0.z, k0.w), pack_bf16x2(k1.x, k1.y), pack_bf16x2(k1.z, k1.w)};
+    const uint4 vb = {pack_bf16x2(v0.x, v0.y), pack_bf16x2(v0.z, v0.w), pack_bf16x2(v1.x, v1.y), pack_bf16x2(v1.z, v1.w)};
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int tv = t0 + c.wave + kWaves * j;
-      vv[j] = tv == c.pos ? vcb : vv[j];
+    for (int j = 0; j < NPASS; ++j) {
+      const bool here = t0 + j * PPP + pg == c.pos;
+      kr[j].x = here ? kb.x : kr[j].x;
+      kr[j].y = here ? kb.y : kr[j].y;
+      kr[j].z = here ? kb.z : kr[j].z;
+      kr[j].w = here ? kb.w : kr[j].w;
+      vr[j].x = here ? vb.x : vr[j].x;
+      vr[j].y = here ? vb.y : vr[j].y;
+      vr[j].z = here ? vb.z : vr[j].z;
+      vr[j].w = here ? vb.w : vr[j].w;
     }
   }
 
-  // heads are an outer, not unrolled loop: unrolling it would let the
-  // scheduler hoist every broadcast read of q into registers at once
-#pragma unroll 1
+  float acc[G][8];
+  float wmax[G], wsum[G];
+#pragma unroll
   for (int h = 0; h < G; ++h) {
-    float a = 0.f;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const uint4 w = kr[q];
-      const float4 qa = *reinterpret_cast<const float4*>(qs + h * D + dq + q * 8);
-      const float4 qb = *reinterpret_cast<const float4*>(qs + h * D + dq + q * 8 + 4);
-      a = fmaf(qa.x, bf_lo(w.x), a); a = fmaf(qa.y, bf_hi(w.x), a);
-      a = fmaf(qa.z, bf_lo(w.y), a); a = fmaf(qa.w, bf_hi(w.y), a);
-      a = fmaf(qb.x, bf_lo(w.z), a); a = fmaf(qb.y, bf_hi(w.z), a);
-      a = fmaf(qb.z, bf_lo(w.w), a); a = fmaf(qb.w, bf_hi(w.w), a);
-    }
-    if (TPP == 2) a += dpp<0xB1>(a);  // the two halves of the position's dims (adjacent lanes)
-    if (scorer && (c.tid % TPP) == 0) sc[sp * G + h] = a;
-  }
-  __syncthreads();
-
-  // softmax statistics of this chunk: wave h owns head h
-  if (c.wave < G) {
-    const int h = c.wave;
+    const float4 qa = *reinterpret_cast<const float4*>(qs + h * D + ds * 8);
+    const float4 qb = *reinterpret_cast<const float4*>(qs + h * D + ds * 8 + 4);
+    float sc[NPASS];
     float m = -__builtin_inff();
-    for (int i = c.lane; i < len; i += 64) m = fmaxf(m, sc[i * G + h]);
+#pragma unroll
+    for (int j = 0; j < NPASS; ++j) {
+      const float a = slice_sum<NT>(dot8r(kr[j], qa, qb));
+      sc[j] = t0 + j * PPP + pg < t1 ? a : -__builtin_inff();
+      m = fmaxf(m, sc[j]);
+    }
     m = wave_max(m);
     float ls = 0.f;
-    for (int i = c.lane; i < len; i += 64) {
-      const float p = __expf(sc[i * G + h] - m);
-      sc[i * G + h] = p;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NPASS; ++j) {
+      const float p = sc[j] == -__builtin_inff() ? 0.f : __expf(sc[j] - m);
       ls += p;
+      const uint4 w = vr[j];
+      acc[h][0] = fmaf(p, bf_lo(w.x), acc[h][0]);
+      acc[h][1] = fmaf(p, bf_hi(w.x), acc[h][1]);
+      acc[h][2] = fmaf(p, bf_lo(w.y), acc[h][2]);
+      acc[h][3] = fmaf(p, bf_hi(w.y), acc[h][3]);
+      acc[h][4] = fmaf(p, bf_lo(w.z), acc[h][4]);
+      acc[h][5] = fmaf(p, bf_hi(w.z), acc[h][5]);
+      acc[h][6] = fmaf(p, bf_lo(w.w), acc[h][6]);
+      acc[h][7] = fmaf(p, bf_hi(w.w), acc[h][7]);
     }
-    ls = wave_sum(ls);
-    if (c.lane == 0) {
-      wm[h] = m;
-      wl[h] = ls;
-    }
+    // every lane of a position group holds the same p: count one slice per group
+    wsum[h] = wave_sum(ds == 0 ? ls : 0.f);
+    wmax[h] = m;
   }
-  __syncthreads();
-
-  float acc[G][DPL];
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
-#pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const int tv = t0 + c.wave + kWaves * j;
-    const bool live = tv < t1;
-    const int slot = live ? tv - t0 : 0;  // in-bounds read, masked below
-    float v[DPL];
-    v[0] = bf_lo(vv[j]);
-    if (DPL == 2) v[DPL - 1] = bf_hi(vv[j]);
-    float pr[G];
-    if (G == 4) {
-      const float4 q4 = *reinterpret_cast<const float4*>(sc + slot * G);
-      pr[0] = q4.x; pr[G > 1 ? 1 : 0] = q4.y; pr[G > 2 ? 2 : 0] = q4.z; pr[G > 3 ? 3 : 0] = q4.w;
-    } else if (G == 2) {
-      const float2 q2 = *reinterpret_cast<const float2*>(sc + slot * G);
-      pr[0] = q2.x; pr[G > 1 ? 1 : 0] = q2.y;
-    } else {
-      pr[0] = sc[slot * G];
-    }
+    for (int e = 0; e < 8; ++e) acc[h][e] = group_sum<NT>(acc[h][e]);
+  if (c.lane < NT) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float p = live ? pr[h] : 0.f;
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[h][e] = fmaf(p, v[e], acc[h][e]);
+      float* dst = wpart + (c.wave * G + h) * D + ds * 8;
+      *reinterpret_cast<float4*>(dst) = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
     }
   }
+  if (c.lane == 0) {
 #pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) wpart[(c.wave * G + h) * D + c.lane * DPL + e] = acc[h][e];
+    for (int h = 0; h < G; ++h) {
+      wm[c.wave * G + h] = wmax[h];
+      wl[c.wave * G + h] = wsum[h];
+    }
+  }
   mark_wave(c);
   __syncthreads();
   mark(c, 2);
 
+  // merge the waves in order: max, then rescaled sums
   const int h = c.tid / D, d = c.tid % D;
-  float a = 0.f, lh = 0.f, mh = 0.f;
+  float A = 0.f, Ls = 0.f, M = -__builtin_inff();
   if (c.tid < G * D) {
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) a += wpart[(w * G + h) * D + d];
-    lh = wl[h];
-    mh = wm[h];
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wm[w * G + h]);
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = wm[w * G + h];
+      const float e = mw == -__builtin_inff() ? 0.f : __expf(mw - M);
+      A = fmaf(e, wpart[(w * G + h) * D + d], A);
+      Ls = fmaf(e, wl[w * G + h], Ls);
+    }
   }
   uint64_t* o = P.o + (size_t)l * P.QD + (size_t)g * G * D;
   if (C == 1) {
-    if (c.tid < G * D) st_tag(o + c.tid, a / lh, c.epoch);
+    if (c.tid < G * D) st_tag(o + c.tid, A / Ls, c.epoch);
     return true;
   }
   // publish this chunk's partial {m[G], l[G], acc[G][D]}; the last chunk of the head merges
   const int stride = G * (D + 2);
   float* mine = P.attn_part + (((size_t)l * P.NKV + g) * C + ch) * stride;
-  if (c.tid < G * D) st_f32_agent(mine + 2 * G + c.tid, a);
+  if (c.tid < G * D) st_f32_agent(mine + 2 * G + c.tid, A);
   if (c.tid < G * D && d == 0) {
-    st_f32_agent(mine + h, mh);
-    st_f32_agent(mine + G + h, lh);
+    st_f32_agent(mine + h, M);
+    st_f32_agent(mine + G + h, Ls);
   }
   wait_all_vmem();
   __syncthreads();
@@ -985,17 +979,17 @@ __device__ __forceinline__ bool attn_task(const Params& P, Ctx& c, const Task& t
   __syncthreads();
   if (c.flags[1] && c.tid < G * D) {
     const float* base = P.attn_part + ((size_t)l * P.NKV + g) * C * stride;
-    float M = -__builtin_inff();
-    for (int k = 0; k < C; ++k) M = fmaxf(M, ld_f32_agent(base + (size_t)k * stride + h));
-    float Ls = 0.f, A = 0.f;
+    float MM = -__builtin_inff();
+    for (int k = 0; k < C; ++k) MM = fmaxf(MM, ld_f32_agent(base + (size_t)k * stride + h));
+    float LL = 0.f, AA = 0.f;
     for (int k = 0; k < C; ++k) {
       const float* pk = base + (size_t)k * stride;
       const float mk = ld_f32_agent(pk + h);
-      const float e = mk == -__builtin_inff() ? 0.f : __expf(mk - M);
-      Ls = fmaf(e, ld_f32_agent(pk + G + h), Ls);
-      A = fmaf(e, ld_f32_agent(pk + 2 * G + c.tid), A);
+      const float e = mk == -__builtin_inff() ? 0.f : __expf(mk - MM);
+      LL = fmaf(e, ld_f32_agent(pk + G + h), LL);
+      AA = fmaf(e, ld_f32_agent(pk + 2 * G + c.tid), AA);
     }
-    st_tag(o + c.tid, A / Ls, c.epoch);
+    st_tag(o + c.tid, AA / LL, c.epoch);
   }
   return true;
 }

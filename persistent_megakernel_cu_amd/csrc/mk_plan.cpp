@@ -161,9 +161,9 @@ int plan_build(const mk_config& c, int W, Plan& p) {
   for (const Task& t : p.tape) p.num_tasks += t.op != OP_NONE;
 
   // ---- LDS layout
-  // attention scratch: q [G][D], k and v of this step [D] each, scores
-  // [kMaxChunk][G], per-wave partial outputs [waves][G][D], head max and sum
-  const int attn_floats = p.G * p.D + 2 * p.D + kMaxChunk * p.G + kWaves * p.G * p.D + 2 * kMaxGroup;
+  // attention scratch: q [G][D], k and v of this step [D] each, per-wave
+  // partial outputs [waves][G][D], per-wave max and sum [waves][G] each
+  const int attn_floats = p.G * p.D + 2 * p.D + kWaves * p.G * p.D + 2 * kWaves * p.G;
   p.act_floats = round_up(std::max(std::max(p.Hp, p.QDp), std::max(p.Fp, attn_floats)), 4);
   p.res_floats = round_up(std::max(max_res_rows, 4), 4);
   if (max_res_rows > kThreads) return fail(p, MK_E_UNSUPPORTED, "more than 512 residual rows per workgroup");
