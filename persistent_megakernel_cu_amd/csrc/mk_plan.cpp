@@ -118,14 +118,19 @@ int plan_build(const mk_config& c, int W, Plan& p) {
   p.stages = kStagesPerLayer * p.L + 1;
   p.tape.assign((size_t)p.stages * W, Task{});
   int max_res_rows = 0;
-  auto gemv_stage = [&](int s, Op op, int layer, uint64_t pairs, uint32_t nu, uint64_t wofs, uint8_t region) {
+  // Row pairs of a GEMV stage in contiguous, balanced ranges over workgroups
+  // [b0, W).
+  auto gemv_stage = [&](int s, Op op, int layer, uint64_t pairs, uint32_t nu, uint64_t wofs, uint8_t region,
+                        int b0 = 0) {
+    const int nw = W - b0;
     uint32_t n = 0;
-    for (int b = 0; b < W; ++b) {
-      uint64_t a0 = pairs * (uint64_t)b / W, a1 = pairs * (uint64_t)(b + 1) / W;
+    for (int i = 0; i < nw; ++i) {
+      uint64_t a0 = pairs * (uint64_t)i / nw, a1 = pairs * (uint64_t)(i + 1) / nw;
       if (a1 > a0) ++n;
     }
-    for (int b = 0; b < W; ++b) {
-      uint64_t a0 = pairs * (uint64_t)b / W, a1 = pairs * (uint64_t)(b + 1) / W;
+    for (int i = 0; i < nw; ++i) {
+      const int b = b0 + i;
+      uint64_t a0 = pairs * (uint64_t)i / nw, a1 = pairs * (uint64_t)(i + 1) / nw;
       Task& t = p.tape[(size_t)s * W + b];
       if (a1 == a0) continue;
       t.op = op;
@@ -153,7 +158,11 @@ int plan_build(const mk_config& c, int W, Plan& p) {
       t.ntasks = (uint32_t)(p.NKV * C);
     }
     gemv_stage(s0 + 2, OP_OPROJ, l, p.H / 2, (uint32_t)(2 * p.QDp / kUnitElems), p.off_o[l], 0);
-    gemv_stage(s0 + 3, OP_GU, l, p.F, (uint32_t)(2 * p.Hp / kUnitElems), p.off_gu[l], 0);
+    // When attention occupies few workgroups they sit out the gate/up stage:
+    // they reach it last (after attention and O-proj), and the down
+    // projection waits for the slowest gate/up task.
+    const int gu_b0 = (p.NKV * C * 8 <= W) ? p.NKV * C : 0;
+    gemv_stage(s0 + 3, OP_GU, l, p.F, (uint32_t)(2 * p.Hp / kUnitElems), p.off_gu[l], 0, gu_b0);
     gemv_stage(s0 + 4, OP_DOWN, l, p.H / 2, (uint32_t)(2 * p.Fp / kUnitElems), p.off_down[l], 0);
   }
   gemv_stage(p.stages - 1, OP_LM, p.L, p.V / 2, (uint32_t)(2 * p.Hp / kUnitElems), 0, 1);
