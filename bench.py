@@ -1,16 +1,19 @@
 #!/usr/bin/env python3
-"""Decode benchmark: us/token of batch-1 greedy decode at the Llama-1B shape on
-one MI355X, with the achieved HBM bandwidth of the megakernel against the
-8 TB/s peak, the launch-per-stage and hipGraph baselines, and the CPU oracle.
+"""Decode benchmark: us/token of greedy decode on one MI355X, with the
+achieved HBM bandwidth of the megakernel against the 8 TB/s peak, the
+launch-per-stage and hipGraph baselines, and the CPU oracle.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama1b]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-Workload (llama1b): 16 layers, hidden 2048, 32 query / 8 KV heads of 64, SwiGLU
-8192, vocab 128256, tied embedding, RoPE theta 5e5, bf16 weights ~N(0, 0.02)
-from seed 0.  A 128-token seeded prompt is prefilled through the model
-(untimed), W warm-up steps run, then K greedy steps are timed from position
-128 with the token chained on the device (out_token of step i is d_token of
-step i+1).  Prints one JSON line.
+Default workload (llama1b): 16 layers, hidden 2048, 32 query / 8 KV heads of
+64, SwiGLU 8192, vocab 128256, tied embedding, RoPE theta 5e5, bf16 weights
+~N(0, 0.02) from seed 0.  A 128-token seeded prompt is prefilled through the
+model (untimed), W warm-up steps run, then K greedy steps are timed from
+position 128 with the token chained on the device (out_token of step i is
+d_token of step i+1).  Other workloads: llama1b-long (single steps at
+positions 4096 and 8191 over a seeded 8192-slot cache, each repeated K
+times) and llama8b (K greedy steps from position 2048 over a seeded cache).
+Prints one JSON line.
 """
 
 from __future__ import annotations
@@ -82,58 +85,104 @@ def cpu_cores() -> int:
         return os.cpu_count() or 1
 
 
-def time_mode(mk, torch, shape, wdev, mode, prompt, warmup, steps, max_seq, start_pos, attn_chunks=0):
-    """Prefill, warm up, then time `steps` chained greedy steps. Returns (ms/step, tokens)."""
-    eng = mk.Engine(shape, wdev, max_seq, mode=mode, attn_chunks=attn_chunks)
-    dims = (1, shape.n_layers, shape.n_kv_heads, max_seq, shape.head_dim)
-    k = torch.zeros(dims, dtype=torch.int16, device="cuda")
-    v = torch.zeros(dims, dtype=torch.int16, device="cuda")
-    logits = torch.empty((1, shape.vocab), dtype=torch.float32, device="cuda")
-    tok = torch.empty(1, dtype=torch.int32, device="cuda")
+def device_cache(torch, shape, batch, max_seq, seeded_filled):
+    """K and V caches on the device: zeros, or seeded N(0,1) bf16 in [0, filled)."""
+    import numpy as np
+
+    from synth_inputs import make_kv_cache
+
+    dims = (batch, shape.n_layers, shape.n_kv_heads, max_seq, shape.head_dim)
+    if seeded_filled <= 0:
+        z = torch.zeros(dims, dtype=torch.int16, device="cuda")
+        return z, torch.zeros_like(z)
+    kc, vc = make_kv_cache(shape, batch, max_seq, seeded_filled, master=0)
+    return (torch.from_numpy(kc.view(np.int16)).cuda(), torch.from_numpy(vc.view(np.int16)).cuda())
+
+
+def time_mode(mk, torch, wl, wdev, mode, warmup, steps, max_seq, attn_chunks=0):
+    """One engine in `mode` on workload `wl`.
+
+    Chained workloads (a prompt, or a seeded cache and a start token) run
+    `warmup` greedy steps, then `steps` timed greedy steps whose input token is
+    the previous step's out_token on the device.  The long-context workload
+    times `steps` repeats of one step at each of its positions (the step is
+    idempotent: same token, same slot written).  Returns (ms per step, tokens
+    of an untimed replay, per-position ms).
+    """
+    from synth_inputs import make_prompt, make_start_token
+
+    shape, B = wl.shape, wl.batch
+    eng = mk.Engine(shape, wdev, max_seq, mode=mode, batch=B, attn_chunks=attn_chunks)
+    k, v = device_cache(torch, shape, B, max_seq, wl.cache_filled)
+    logits = torch.empty((B, shape.vocab), dtype=torch.float32, device="cuda")
+    tok = torch.empty(B, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
-    # prefill the prompt (untimed); the last step's argmax is the first decode input
-    for p, t in enumerate(prompt):
-        tok.fill_(int(t))
-        eng.decode_step(tok, p, k, v, logits, tok, stream)
-    torch.cuda.synchronize()
-    first = tok.clone()
-    for i in range(warmup):
-        eng.decode_step(tok, start_pos + i, k, v, logits, tok, stream)
-    torch.cuda.synchronize()
-    tok.copy_(first)
-    toks = torch.empty(steps, dtype=torch.int32, device="cuda")
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    per_pos = {}
+    if wl.prompt_len > 0:
+        for p, t in enumerate(make_prompt(shape, wl.prompt_len, master=0)):
+            tok.fill_(int(t))
+            eng.decode_step(tok, p, k, v, logits, tok, stream)
+    else:
+        tok.copy_(torch.tensor([make_start_token(shape, b) for b in range(B)], dtype=torch.int32))
     torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(steps):
-        eng.decode_step(tok, start_pos + i, k, v, logits, tok, stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1)
-    # replay once more, recording tokens, to compare modes (untimed)
-    tok.copy_(first)
-    for i in range(steps):
-        eng.decode_step(tok, start_pos + i, k, v, logits, tok, stream)
-        toks[i : i + 1].copy_(tok)
-    torch.cuda.synchronize()
+    first = tok.clone()
+    if wl.name == "llama1b-long":
+        out = torch.empty_like(tok)
+        for pos in (wl.start_pos, wl.max_seq - 1):
+            for _ in range(warmup):
+                eng.decode_step(first, pos, k, v, logits, out, stream)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(steps):
+                eng.decode_step(first, pos, k, v, logits, out, stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            per_pos[pos] = e0.elapsed_time(e1) / steps
+        toks = [int(x) for x in out.cpu().tolist()]
+        ms = sum(per_pos.values()) / len(per_pos)
+    else:
+        start = wl.start_pos
+        for i in range(warmup):
+            eng.decode_step(tok, start + i, k, v, logits, tok, stream)
+        torch.cuda.synchronize()
+        tok.copy_(first)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(steps):
+            eng.decode_step(tok, start + i, k, v, logits, tok, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        # replay once more, recording tokens, to compare modes (untimed)
+        tok.copy_(first)
+        rec = torch.empty((steps, B), dtype=torch.int32, device="cuda")
+        for i in range(steps):
+            eng.decode_step(tok, start + i, k, v, logits, tok, stream)
+            rec[i].copy_(tok)
+        torch.cuda.synchronize()
+        toks = rec.cpu().tolist()
     st = eng.status()
     eng.close()
     if st.code != 0:
         raise RuntimeError(f"{mode}: device status {st.code} (stage {st.stage}, wg {st.wg})")
-    return ms / steps, toks.cpu().tolist()
+    return ms, toks, per_pos
 
 
-def cpu_baseline(shape, weights, start_pos: int, budget_s: float = 12.0):
-    """Time the oracle on a bounded sample of the same workload."""
+def cpu_baseline(wl, weights, budget_s: float = 12.0):
+    """Time the oracle on a bounded sample of the same workload (sequence 0)."""
     import numpy as np
 
     import oracle as orc
     from synth_inputs import make_kv_cache, make_start_token
 
-    o = orc.Oracle(shape, weights)
-    cap = 1024
-    kc, vc = make_kv_cache(shape, 1, start_pos + cap, start_pos, master=0)
+    shape = wl.shape
+    start_pos = wl.start_pos
+    o = orc.Oracle(shape, weights, lazy=shape.n_layers * shape.hidden > 16 * 2048)
+    cap = 1024 if wl.prompt_len > 0 else 64
+    filled = wl.cache_filled if wl.cache_filled > 0 else start_pos
+    kc, vc = make_kv_cache(shape, 1, max(wl.max_seq, start_pos + cap), filled, master=0)
     kc, vc = kc[0], vc[0]
     tok = make_start_token(shape, 0)
     n = 0
@@ -142,7 +191,7 @@ def cpu_baseline(shape, weights, start_pos: int, budget_s: float = 12.0):
         lg = o.decode_step(tok, start_pos + n, kc, vc)
         tok = int(np.argmax(lg))
         n += 1
-        if (time.perf_counter() - t0 > budget_s and n >= 2) or n >= cap:
+        if time.perf_counter() - t0 > budget_s or n >= cap or start_pos + n >= kc.shape[2]:
             break
     dt = time.perf_counter() - t0
     return {
@@ -150,9 +199,10 @@ def cpu_baseline(shape, weights, start_pos: int, budget_s: float = 12.0):
         "unit": "µs/token",
         "cores": cpu_cores(),
         "kind": "oracle",
-        "sample": f"{n} greedy decode steps at positions {start_pos}..{start_pos + n - 1} over a cache whose "
-                  f"first {start_pos} slots are seeded N(0,1) bf16 (same cost as the prefilled prompt); "
-                  f"NumPy fp32 with weights widened before timing",
+        "sample": f"{n} greedy decode step(s) of sequence 0 at positions {start_pos}..{start_pos + n - 1} over a "
+                  f"cache whose first {filled} slots are seeded N(0,1) bf16 (for a prefilled prompt: the same "
+                  f"cost as the prompt's own K/V); NumPy fp32"
+                  + (", each matrix widened to fp32 inside the step" if o.lazy else ", weights widened before timing"),
     }
 
 
@@ -192,36 +242,45 @@ def main() -> int:
     import torch
 
     import persistent_megakernel_cu_amd.binding as mk
-    from synth_inputs import WORKLOADS, make_prompt, make_weights
+    from synth_inputs import WORKLOADS, make_weights
 
     wl = WORKLOADS[args.workload]
     shape = wl.shape
-    if wl.prompt_len <= 0:
-        print(json.dumps({"error": f"workload {wl.name} is a parity case, not a bench line"}))
+    if wl.steps <= 0:
+        print(json.dumps({"error": f"workload {wl.name} has no decode steps to time"}))
         return 2
-    start = wl.prompt_len
     steps = args.steps
-    max_seq = max(wl.max_seq, start + max(steps, args.warmup))
+    max_seq = wl.max_seq if wl.name == "llama1b-long" else max(wl.max_seq, wl.start_pos + max(steps, args.warmup))
     t0 = time.time()
     weights = make_weights(shape, master=0)
     wdev = mk.to_device(weights)
-    prompt = make_prompt(shape, wl.prompt_len, master=0)
-    print(f"[bench] weights ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    print(f"[bench] {wl.name}: weights ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
-    results = {}
-    tokens = {}
+    results, tokens, per_pos = {}, {}, {}
     for mode in args.modes.split(","):
-        ms, toks = time_mode(mk, torch, shape, wdev, mode, prompt, args.warmup, steps, max_seq, start,
-                             args.attn_chunks)
-        results[mode] = ms
-        tokens[mode] = toks
+        ms, toks, pp = time_mode(mk, torch, wl, wdev, mode, args.warmup, steps, max_seq, args.attn_chunks)
+        results[mode], tokens[mode], per_pos[mode] = ms, toks, pp
         print(f"[bench] {mode}: {ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
 
     main_mode = "mega" if "mega" in results else next(iter(results))
     ms = results[main_mode]
-    us_tok = ms * 1e3
-    avg_bytes = sum(algorithmic_bytes(shape, start + i) for i in range(steps)) / steps
+    B = wl.batch
+    us_tok = ms * 1e3 / B
+    if wl.name == "llama1b-long":
+        positions = sorted(per_pos[main_mode])
+        avg_bytes = sum(algorithmic_bytes(shape, p, B) for p in positions) / len(positions)
+        where = (f"single steps at positions {', '.join(map(str, positions))} over a seeded {wl.max_seq}-slot "
+                 f"N(0,1) bf16 cache, each repeated {steps} times (same token, idempotent)")
+    else:
+        positions = list(range(wl.start_pos, wl.start_pos + steps))
+        avg_bytes = sum(algorithmic_bytes(shape, p, B) for p in positions) / steps
+        where = (f"positions {wl.start_pos}..{wl.start_pos + steps - 1} "
+                 + (f"after a {wl.prompt_len}-token prefill" if wl.prompt_len > 0
+                    else f"over a seeded {wl.cache_filled}-slot N(0,1) bf16 cache"))
     achieved = avg_bytes / (ms * 1e-3) / 1e9
+    sh = shape
+    model = (f"{sh.n_layers}L, H{sh.hidden}, {sh.n_heads}q/{sh.n_kv_heads}kv x{sh.head_dim}, SwiGLU {sh.ffn}, "
+             f"V{sh.vocab}, {'tied' if sh.tie_embeddings else 'untied'}")
     out = {
         "metric": METRIC,
         "value": round(us_tok, 2),
@@ -236,10 +295,9 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": f"{wl.name}: batch-1 greedy decode, Llama-1B shape (16L, H2048, 32q/8kv x64, "
-                        f"SwiGLU 8192, V128256, tied), bf16 weights and KV cache, fp32 accumulate, "
-                        f"positions {start}..{start + steps - 1} after a {start}-token prefill",
-            "batch": 1,
+            "workload": f"{wl.name}: batch-{B} greedy decode, {sh.name} shape ({model}), bf16 weights and KV "
+                        f"cache, fp32 activations and accumulation, {where}",
+            "batch": B,
             "weights": "bf16 ~N(0,0.02) seed 0",
             "tokens_per_s": round(1e6 / us_tok, 1),
             "parallelism": "single GPU",
@@ -254,14 +312,16 @@ def main() -> int:
             "bytes_per_step": int(avg_bytes),
             "traffic_unit": "HBM bytes per launch (one launch = one decode step)",
         },
-        "baselines": {m: {"us_per_token": round(v * 1e3, 2), "tokens_per_s": round(1e3 / v, 1)}
+        "baselines": {m: {"us_per_token": round(v * 1e3 / B, 2), "tokens_per_s": round(B * 1e3 / v, 1)}
                       for m, v in results.items()},
         "modes_agree": all(t == tokens[main_mode] for t in tokens.values()),
     }
+    if per_pos[main_mode]:
+        out["per_position_us"] = {str(p): round(t * 1e3, 2) for p, t in sorted(per_pos[main_mode].items())}
     if "graph" in results and "mega" in results:
         out["speedup_vs_graph"] = round(results["graph"] / results["mega"], 3)
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(shape, weights, start)
+        out["cpu_baseline"] = cpu_baseline(wl, weights)
     print(json.dumps(out), flush=True)
     return 0
 

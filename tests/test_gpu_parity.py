@@ -147,3 +147,53 @@ def test_error_paths(tiny_w):
         assert out == int(np.argmax(lg))
     finally:
         gpu.close()
+
+
+@pytest.mark.skip(reason="the first run of the Llama-8B shape (head_dim 128, hidden 4096) faulted the GPU; the "
+                         "cause is not found yet and mk_load refuses head_dim 128 / hidden > 2048 until it is")
+def test_llama8b_seeded_cache():
+    # Llama-8B shape (head_dim 128, untied LM head) over a seeded 2048-slot
+    # cache: two teacher-forced steps at positions 2048 and 2049
+    import time
+
+    from synth_inputs import LLAMA_8B
+
+    sh = LLAMA_8B
+    t0 = time.time()
+    w = make_weights(sh, master=0)
+    log(f"[8b] weights generated in {time.time() - t0:.0f}s")
+    kv = make_kv_cache(sh, 1, 2112, 2048, master=0)
+    o = orc.Oracle(sh, w, lazy=True)
+    gpu = GpuDecoder(sh, w, 2112, mode="mega", kv_init=kv)
+    log(f"[8b] engine loaded at {time.time() - t0:.0f}s")
+    kc, vc = kv[0][0].copy(), kv[1][0].copy()
+    tok = make_start_token(sh, 0)
+    try:
+        for pos in (2048, 2049):
+            lg, out = gpu.step(tok, pos)
+            lg_ref = o.decode_step(tok, pos, kc, vc)
+            err = float(np.max(np.abs(lg.astype(np.float64) - lg_ref)))
+            log(f"[parity] llama8b pos={pos} err/tol={err / logit_tol(lg_ref):.3g} at {time.time() - t0:.0f}s")
+            assert err <= logit_tol(lg_ref)
+            assert out == int(np.argmax(lg))
+            ref_tok = orc.argmax_first(lg_ref)
+            srt = np.sort(lg_ref)
+            assert out == ref_tok or srt[-1] - srt[-2] < logit_tol(lg_ref)
+            tok = ref_tok
+    finally:
+        gpu.close()
+
+
+def test_llama8b_shape_refused():
+    # mk_load refuses head_dim 128 / hidden > 2048 before touching any weight:
+    # placeholder device buffers stand in for the 16 GB of weights
+    import torch
+
+    from persistent_megakernel_cu_amd import binding as mkb
+    from synth_inputs import LLAMA_8B, weight_shapes
+
+    dummy = torch.zeros(16, dtype=torch.int16, device="cuda")
+    w = {name: dummy for name, _, _ in weight_shapes(LLAMA_8B)}
+    with pytest.raises(mkb.MkError) as e:
+        mkb.Engine(LLAMA_8B, w, 2112)
+    assert e.value.code == mkb.MK_E_UNSUPPORTED
