@@ -12,8 +12,10 @@
 #include "mk_plan.h"
 
 namespace mk {
-hipError_t configure_kernels(int G, int D, int lds_bytes);
-hipError_t persistent_occupancy(int G, int D, int lds_bytes, int* blocks_per_cu);
+hipError_t configure_kernels(int G, int D, bool batched, int lds_bytes);
+hipError_t launch_tile_rows(const uint16_t* src, size_t sstride, int nsrc, int kcols, uint16_t* dst, int kp, int row0,
+                            int rstep);
+hipError_t persistent_occupancy(int G, int D, bool batched, int lds_bytes, int* blocks_per_cu);
 hipError_t launch_persistent(const Params& P, int lds_bytes, hipStream_t stream);
 hipError_t launch_stage(const Params& P, int s, int lds_bytes, hipStream_t stream);
 hipError_t launch_set_args(StepArgs* a, int pos, uint32_t epoch, hipStream_t stream);
@@ -151,6 +153,7 @@ Params make_params(mk_handle* h) {
   P.lds_misc = p.lds_misc;
   P.lds_part = p.lds_part;
   P.lds_tape = p.lds_tape;
+  P.act_stride = p.act_stride;
   P.act_floats = p.act_floats;
   P.res_floats = p.res_floats;
   P.watchdog_ticks = h->watchdog_ticks;
@@ -280,16 +283,46 @@ int mk_load(const mk_config* cfg, const mk_weights* w, mk_handle** out) {
   if (p.D != 64 || p.H > 2048) { release(h); return MK_E_UNSUPPORTED; }
 
   // persistent residency: one workgroup per compute unit must fit
-  HIP_OR(mk::configure_kernels(p.G, p.D, p.lds_bytes));
+  HIP_OR(mk::configure_kernels(p.G, p.D, p.batched, p.lds_bytes));
   int per_cu = 0;
-  HIP_OR(mk::persistent_occupancy(p.G, p.D, p.lds_bytes, &per_cu));
+  HIP_OR(mk::persistent_occupancy(p.G, p.D, p.batched, p.lds_bytes, &per_cu));
   if (per_cu < 1) { release(h); return MK_E_DEVICE; }
 
   // packed weights
   if (hipMalloc(&h->arena, p.arena_bytes) != hipSuccess) { (void)hipGetLastError(); release(h); return MK_E_NOMEM; }
   HIP_OR(hipMemset(h->arena, 0, p.arena_bytes));
   const size_t H2 = (size_t)p.H * 2, Hp2 = (size_t)p.Hp * 2;
-  for (int l = 0; l < p.L; ++l) {
+  if (p.batched) {
+    // tiled matrices (16 x 32 tiles in MFMA A-operand lane order); rows are
+    // read 16 bytes at a time, so every source must be 16-byte aligned
+    auto aligned = [](const void* q) { return ((uintptr_t)q & 15u) == 0; };
+    for (int l = 0; l < p.L; ++l) {
+      const mk_layer_weights& lw = w->layers[l];
+      if (!aligned(lw.wq) || !aligned(lw.wk) || !aligned(lw.wv) || !aligned(lw.wo) || !aligned(lw.w_gate) ||
+          !aligned(lw.w_up) || !aligned(lw.w_down)) {
+        release(h);
+        return MK_E_INVAL;
+      }
+    }
+    const uint16_t* lm_src = p.tied ? w->embed : w->lm_head;
+    if (!aligned(lm_src)) { release(h); return MK_E_INVAL; }
+    uint16_t* A = reinterpret_cast<uint16_t*>(h->arena);
+    for (int l = 0; l < p.L; ++l) {
+      const mk_layer_weights& lw = w->layers[l];
+      uint16_t* q = A + p.off_qkv[l] / 2;
+      HIP_OR(mk::launch_tile_rows(lw.wq, p.H, p.QD, p.H, q, p.Hp, 0, 1));
+      HIP_OR(mk::launch_tile_rows(lw.wk, p.H, p.KVD, p.H, q, p.Hp, p.QD, 1));
+      HIP_OR(mk::launch_tile_rows(lw.wv, p.H, p.KVD, p.H, q, p.Hp, p.QD + p.KVD, 1));
+      HIP_OR(mk::launch_tile_rows(lw.wo, p.QD, p.H, p.QD, A + p.off_o[l] / 2, p.QDp, 0, 1));
+      HIP_OR(mk::launch_tile_rows(lw.w_gate, p.H, p.F, p.H, A + p.off_gu[l] / 2, p.Hp, 0, 2));
+      HIP_OR(mk::launch_tile_rows(lw.w_up, p.H, p.F, p.H, A + p.off_gu[l] / 2, p.Hp, 1, 2));
+      HIP_OR(mk::launch_tile_rows(lw.w_down, p.F, p.H, p.F, A + p.off_down[l] / 2, p.Fp, 0, 1));
+    }
+    if (hipMalloc(&h->lm_copy, p.lm_bytes) != hipSuccess) { (void)hipGetLastError(); release(h); return MK_E_NOMEM; }
+    HIP_OR(mk::launch_tile_rows(lm_src, p.H, p.V, p.H, reinterpret_cast<uint16_t*>(h->lm_copy), p.Hp, 0, 1));
+    h->lm = h->lm_copy;
+  }
+  for (int l = 0; l < p.L && !p.batched; ++l) {
     const mk_layer_weights& lw = w->layers[l];
     char* q = h->arena + p.off_qkv[l];
     HIP_OR(hipMemcpy2D(q, Hp2, lw.wq, H2, H2, p.QD, hipMemcpyDeviceToDevice));
@@ -304,7 +337,9 @@ int mk_load(const mk_config* cfg, const mk_weights* w, mk_handle** out) {
                        hipMemcpyDeviceToDevice));
   }
   const uint16_t* lm_src = p.tied ? w->embed : w->lm_head;
-  if (p.lm_borrowed) {
+  if (p.batched) {
+    // tiled above
+  } else if (p.lm_borrowed) {
     h->lm = reinterpret_cast<const char*>(lm_src);
   } else {
     if (hipMalloc(&h->lm_copy, p.lm_bytes) != hipSuccess) { (void)hipGetLastError(); release(h); return MK_E_NOMEM; }

@@ -26,8 +26,20 @@ constexpr int kRing = 8;
 constexpr int kMaxGroup = 8;
 // Largest number of split items (pairs << kslog) of one task (LDS partials).
 constexpr int kMaxItems = 256;
-// Longest attention chunk (positions) one task handles.
+// Positions one attention task holds in registers at a time; a task of a
+// batched plan walks its chunk in blocks of this many positions.
 constexpr int kMaxChunk = 256;
+
+// Batched decode (2..kMaxBatch sequences): every matrix is stored as tiles of
+// kTileRows rows x kTileCols columns, one 1 KiB unit per tile in the lane
+// order of a 16x16x32 bf16 MFMA A operand (lane l holds row l % 16, columns
+// 8 * (l / 16) .. +8); activations of the batch form the B operand.
+constexpr int kMaxBatch = 8;
+constexpr int kTileRows = 16;
+constexpr int kTileCols = 32;
+// Columns of an activation chunk held in LDS at once (per sequence).
+constexpr int kChunkCols = 2048;
+constexpr int kChunkTiles = kChunkCols / kTileCols;
 
 // Stage kinds, in their order within a layer; the LM head closes the tape.
 enum Op : uint8_t {
@@ -52,7 +64,10 @@ constexpr int kStagesPerLayer = 5;
 //            is the whole pair and one wave finishes it; otherwise an item is
 //            a run of nu >> kslog units inside one row, and the partial sums
 //            of a pair's items are added in LDS in item order.
-//  OP_ATTN : a0 = kv head, a1 = chunk index.
+//  OP_ATTN : a0 = kv head, a1 = chunk index, nu = sequence of the batch.
+//  Batched plans: GEMM tasks cover row blocks [a0, a1) of 16 rows; nu is the
+//            number of 32-column tiles of a row; each block's tiles are cut
+//            into 2^kslog parts (split over waves, summed in LDS).
 struct Task {
   uint8_t op;
   uint8_t region;
@@ -124,6 +139,7 @@ struct Params {
   int32_t lds_misc;      // reductions and flags
   int32_t lds_part;      // [kMaxItems] partial sums of split items
   int32_t lds_tape;      // this workgroup's task records, one per stage
+  int32_t act_stride;    // batched: floats per sequence in the activation chunk
   int32_t act_floats;
   int32_t res_floats;
 

@@ -455,6 +455,7 @@ struct Stream {
   int issued, consumed, lslot, cslot;
   int ls, s_begin, s_end;
   uint32_t litem, lnitems, lkslog, lupi, lu, la0, lnu;
+  uint32_t lc, lnc, lch;  // batched: chunk, chunks per row, tiles per chunk
   const char* lbase;
   bool ldone;
 };
@@ -995,12 +996,698 @@ __device__ __forceinline__ bool attn_task(const Params& P, Ctx& c, const Task& t
 }
 
 // ---------------------------------------------------------------------------
+// batched decode (2..8 sequences): tiled weights, bf16 MFMA with the batch
+// as the N operand
+// ---------------------------------------------------------------------------
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Sequence n's slice of a [B][L][len] activation buffer.
+__device__ __forceinline__ size_t seq_off(const Params& P, int n, int l, int len) {
+  return ((size_t)n * P.L + l) * (size_t)len;
+}
+
+// Loader of a batched stream: items wave, wave + 8, ... of (a1 - a0) << kslog
+// (block a0 + (i >> kslog), part i & (2^kslog - 1)); per chunk of ch tiles a
+// part covers tiles [part * upc, + upc) of the chunk, upc = ch >> kslog.
+// Order: chunk, then the wave's items, then tiles.
+__device__ __forceinline__ void loader_seek_b(const Params& P, Stream& st, int s, int wave) {
+  for (; s < st.s_end; ++s) {
+    const Task t = task_at(st.tape, s - st.s_begin);
+    if (op_is_gemv(t.op)) {
+      const uint32_t n_items = (t.a1 - t.a0) << t.kslog;
+      if ((uint32_t)wave < n_items) {
+        const uint32_t ch = t.nu < (uint32_t)kChunkTiles ? t.nu : (uint32_t)kChunkTiles;
+        st.ls = s;
+        st.litem = (uint32_t)wave;
+        st.lnitems = n_items;
+        st.lkslog = t.kslog;
+        st.lupi = ch >> t.kslog;  // tiles per part and chunk
+        st.lu = 0;
+        st.la0 = t.a0;
+        st.lnu = t.nu;            // tiles per row
+        st.lc = 0;
+        st.lnc = t.nu / ch;
+        st.lch = ch;
+        st.lbase = (t.region ? P.lm : P.arena) + t.wofs;
+        return;
+      }
+    }
+  }
+  st.ls = st.s_end;
+  st.ldone = true;
+}
+
+__device__ __forceinline__ void loader_issue_b(const Params& P, Stream& st, int wave, int lane) {
+  if (st.ldone) return;
+  const uint32_t block = st.la0 + (st.litem >> st.lkslog);
+  const uint32_t part = st.litem & ((1u << st.lkslog) - 1u);
+  const uint32_t kb = st.lc * st.lch + part * st.lupi + st.lu;
+  const char* g = st.lbase + ((uint64_t)block * st.lnu + kb) * kUnitBytes + (uint32_t)lane * 16u;
+  dma_unit(g, st.ring + (uint32_t)st.lslot * kUnitBytes);
+  ++st.issued;
+  st.lslot = (st.lslot + 1 == kRing) ? 0 : st.lslot + 1;
+  if (++st.lu == st.lupi) {
+    st.lu = 0;
+    st.litem += kWaves;
+    if (st.litem >= st.lnitems) {
+      st.litem = (uint32_t)wave;
+      if (++st.lc == st.lnc) loader_seek_b(P, st, st.ls + 1, wave);
+    }
+  }
+}
+
+__device__ __forceinline__ void top_up_b(const Params& P, Stream& st, int wave, int lane, int max) {
+  while (max-- > 0 && !st.ldone && st.issued - st.consumed < kRing) loader_issue_b(P, st, wave, lane);
+}
+
+// Next four tiles of the stream (all issued: the ring is refilled on consume).
+__device__ __forceinline__ void take4_b(const Params& P, Stream& st, int wave, int lane, uint4 (&v)[4]) {
+  if (st.issued - st.consumed == kRing)
+    wait_vm<kRing - 4>();
+  else
+    wait_vm<0>();
+  uint32_t a[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    int sl = st.cslot + k;
+    sl = sl >= kRing ? sl - kRing : sl;
+    a[k] = st.ring + (uint32_t)sl * kUnitBytes + (uint32_t)lane * 16u;
+  }
+  lds_read4(v, a);
+  st.consumed += 4;
+  st.cslot = st.cslot + 4 >= kRing ? st.cslot + 4 - kRing : st.cslot + 4;
+  top_up_b(P, st, wave, lane, 4);
+}
+
+__device__ __forceinline__ uint4 take1_b(const Params& P, Stream& st, int wave, int lane) {
+  const uint32_t a = st.ring + (uint32_t)st.cslot * kUnitBytes + (uint32_t)lane * 16u;
+  const uint4 v = (st.issued - st.consumed == kRing) ? ring_read<kRing - 1>(a) : ring_read<0>(a);
+  ++st.consumed;
+  st.cslot = (st.cslot + 1 == kRing) ? 0 : st.cslot + 1;
+  top_up_b(P, st, wave, lane, 1);
+  return v;
+}
+
+// Stage columns [k0, k0 + kc) of B tagged sequences into LDS:
+// dst[n * stride + k] = src_n[k0 + k], src_n = base + n * sstride.  The first
+// round's loads are in flight before the barrier that separates these LDS
+// writes from the previous task's reads.  Ends with a barrier.
+__device__ __forceinline__ bool stage_batch(const Params& P, Ctx& c, float* dst, int stride, const uint64_t* base,
+                                            size_t sstride, int k0, int kc, int kpad, int stage) {
+  const int total = P.B * kc;
+  bool stop = false;
+  for (int i0 = 0; i0 == 0 || i0 < total; i0 += kThreads * kStageLoads) {
+    uint64_t w[kStageLoads];
+#pragma unroll
+    for (int j = 0; j < kStageLoads; ++j) {
+      const int i = i0 + j * kThreads + c.tid;
+      const int n = i < total ? i / kc : 0, k = i - n * kc;
+      w[j] = i < total ? ld_tag(base + (size_t)n * sstride + k0 + k) : ((uint64_t)c.epoch << 32);
+    }
+    uint64_t t0 = 0;
+    while (!stop) {
+      bool ready = true;
+#pragma unroll
+      for (int j = 0; j < kStageLoads; ++j) ready &= (uint32_t)(w[j] >> 32) == c.epoch;
+      if (ready) break;
+      if (poll_stop(P, t0, stage, (uint32_t)(w[0] >> 32))) {
+        stop = true;
+        break;
+      }
+#pragma unroll
+      for (int j = 0; j < kStageLoads; ++j) {
+        const int i = i0 + j * kThreads + c.tid;
+        if (i < total && (uint32_t)(w[j] >> 32) != c.epoch) {
+          const int n = i / kc, k = i - n * kc;
+          w[j] = ld_tag(base + (size_t)n * sstride + k0 + k);
+        }
+      }
+    }
+    if (i0 == 0) {
+      __syncthreads();
+      // zero the padding columns [kc, kpad) of every sequence
+      const int padw = kpad - kc;
+      for (int i = c.tid; i < P.B * padw; i += kThreads) dst[(i / padw) * stride + kc + i % padw] = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kStageLoads; ++j) {
+      const int i = i0 + j * kThreads + c.tid;
+      if (i < total) {
+        const int n = i / kc, k = i - n * kc;
+        dst[n * stride + k] = __uint_as_float((uint32_t)w[j]);
+      }
+    }
+  }
+  if (stop) c.flags[0] = 1;
+  __syncthreads();
+  return c.flags[0] == 0;
+}
+
+// Input token of sequence n (a bad id latches MK_E_TOKEN, marks the sequence
+// and reads row 0 instead).
+__device__ __forceinline__ int token_of(const Params& P, const Ctx& c, int n, int stage, bool report) {
+  int tok = P.token[n];
+  if (tok < 0 || tok >= P.V) {
+    if (report) {
+      latch_error(P, MK_E_TOKEN, stage, (uint32_t)tok);
+      __hip_atomic_store(&P.tokerr[n], c.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    tok = 0;
+  }
+  return tok;
+}
+
+// RMSNorm of the staged batch: wave n < B computes rs[n] = (mean(x^2) +
+// eps)^(-1/2) over x = dst[n][0, H) and scales dst[n][k] by g[k] (zeroing
+// [H, Hp)), so that W . rmsnorm(x_n) = rs[n] * (W . dst_n).
+__device__ __forceinline__ void norm_batch(const Params& P, Ctx& c, float* dst, int stride, const float* g,
+                                           float* rsb) {
+  if (c.wave < P.B) {
+    float* x = dst + c.wave * stride;
+    float ss = 0.f;
+    for (int k = c.lane; k < P.H; k += 64) ss = fmaf(x[k], x[k], ss);
+    ss = wave_sum(ss);
+    if (c.lane == 0) rsb[c.wave] = rsqrtf(ss / (float)P.H + P.eps);
+    for (int k = c.lane; k < P.Hp; k += 64) x[k] = k < P.H ? x[k] * g[k] : 0.f;
+  }
+  __syncthreads();
+}
+
+// B operand of one tile: lane l holds sequence l % 16 (zero past the batch),
+// columns 8 * (l / 16) .. +8 of the tile, as bf16 hi and lo parts (x = hi +
+// lo to about 16 significant bits), so two MFMAs give an fp32-accurate
+// product with the bf16 weights.
+__device__ __forceinline__ void b_operand(const float* act, int stride, int n, bool live, int col,
+                                          bf16x8& hi, bf16x8& lo) {
+  const float* x = act + (live ? n : 0) * stride + col;
+  const float4 a = *reinterpret_cast<const float4*>(x);
+  const float4 b = *reinterpret_cast<const float4*>(x + 4);
+  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float xv = live ? v[i] : 0.f;
+    const __bf16 h = (__bf16)xv;
+    hi[i] = h;
+    lo[i] = (__bf16)(xv - (float)h);
+  }
+}
+
+__device__ __forceinline__ f32x4 mfma_tile(const uint4 w, const bf16x8& hi, const bf16x8& lo, f32x4 acc) {
+  bf16x8 a;
+  __builtin_memcpy(&a, &w, sizeof(a));
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, hi, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, lo, acc, 0, 0, 0);
+  return acc;
+}
+
+struct LmBestB {
+  float v;
+  int i;
+};
+
+// Outputs of a row pair (rows r, r+1 of the stage's matrix) of sequence n:
+// QKV (RoPE pair / v values) and GU (gate, up) pairs.
+template <int OP>
+__device__ __forceinline__ void epi_pair_b(const Params& P, const Ctx& c, int l, int r, int n, float v0, float v1,
+                                           const float* rsb) {
+  const uint32_t tag = c.epoch;
+  v0 *= rsb[n];
+  v1 *= rsb[n];
+  if (OP == OP_QKV) {
+    if (r < P.QD + P.KVD) {
+      const int rr = r < P.QD ? r : r - P.QD;
+      const int j = rr % P.D;
+      const float cs = c.rope[j], sn = c.rope[j + 1];
+      const float y0 = v0 * cs - v1 * sn;
+      const float y1 = v0 * sn + v1 * cs;
+      if (r < P.QD) {
+        uint64_t* q = P.q + seq_off(P, n, l, P.QD) + r;
+        st_tag(q, y0, tag);
+        st_tag(q + 1, y1, tag);
+      } else {
+        const uint16_t k0 = f32_to_bf16(y0), k1 = f32_to_bf16(y1);
+        const int hk = rr / P.D;
+        uint16_t* dst = P.kcache + ((seq_off(P, n, l, P.NKV) + hk) * P.S + c.pos) * P.D + j;
+        *reinterpret_cast<uint32_t*>(dst) = (uint32_t)k0 | ((uint32_t)k1 << 16);
+        uint64_t* kv = P.kvcur + seq_off(P, n, l, 2 * P.KVD) + rr;
+        st_tag(kv, bf16_to_f32(k0), tag);
+        st_tag(kv + 1, bf16_to_f32(k1), tag);
+      }
+    } else {
+      const int rr = r - P.QD - P.KVD;
+      const int hv = rr / P.D, j = rr % P.D;
+      const uint16_t b0 = f32_to_bf16(v0), b1 = f32_to_bf16(v1);
+      uint16_t* dst = P.vcache + ((seq_off(P, n, l, P.NKV) + hv) * P.S + c.pos) * P.D + j;
+      *reinterpret_cast<uint32_t*>(dst) = (uint32_t)b0 | ((uint32_t)b1 << 16);
+      uint64_t* kv = P.kvcur + seq_off(P, n, l, 2 * P.KVD) + P.KVD + rr;
+      st_tag(kv, bf16_to_f32(b0), tag);
+      st_tag(kv + 1, bf16_to_f32(b1), tag);
+    }
+  } else {  // GU: rows (2f, 2f + 1) = (gate f, up f)
+    const float sg = v0 / (1.0f + __expf(-v0));
+    st_tag(P.h + seq_off(P, n, l, P.F) + (r >> 1), sg * v1, tag);
+  }
+}
+
+// Output of one row r of sequence n: OPROJ / DOWN (residual add) and LM.
+template <int OP>
+__device__ __forceinline__ void epi_row_b(const Params& P, const Ctx& c, const Task& t, int l, int r, int n, float v,
+                                          const float* rsb, LmBestB& best) {
+  if (OP == OP_LM) {
+    v *= rsb[n];
+    P.logits[(size_t)n * P.V + r] = v;
+    if (v > best.v) {
+      best.v = v;
+      best.i = r;
+    }
+  } else {
+    const int nr = (int)(t.a1 - t.a0) * kTileRows;
+    const int k = r - (int)t.a0 * kTileRows;
+    uint64_t* dst = (OP == OP_OPROJ ? P.x_attn : P.x_ffn) + seq_off(P, n, l, P.H) + r;
+    st_tag(dst, c.res[n * nr + k] + v, c.epoch);
+  }
+}
+
+// Argmax stage 2 for the batch: every LM task publishes one key per sequence;
+// the last task to arrive picks each sequence's token.
+__device__ __forceinline__ void lm_finish_b(const Params& P, Ctx& c, const Task& t) {
+  uint64_t* keys = reinterpret_cast<uint64_t*>(c.part);  // [kWaves][16] per-wave keys, then [16] per sequence
+  if (c.tid < P.B) {
+    uint64_t k = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) k = keys[w * 16 + c.tid] > k ? keys[w * 16 + c.tid] : k;
+    __hip_atomic_store(&P.amax[(size_t)c.tid * P.num_wgs + c.b], k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  wait_all_vmem();
+  __syncthreads();
+  if (c.tid == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(P.amax_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    c.flags[1] = old == c.epoch * t.ntasks - 1u;
+  }
+  __syncthreads();
+  if (c.flags[1] && c.wave < P.B) {
+    const int n = c.wave;
+    uint64_t k = 0;
+    for (int w = c.lane; w < P.num_wgs; w += 64) {
+      const uint64_t x = ld_tag(P.amax + (size_t)n * P.num_wgs + w);
+      k = x > k ? x : k;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const uint64_t y = __shfl_xor(k, o);
+      k = y > k ? y : k;
+    }
+    if (c.lane == 0) {
+      int idx = k ? (int)(~(uint32_t)k) : -1;
+      if (ld_u32_agent(P.tokerr + n) == c.epoch) idx = -1;
+      P.out_token[n] = idx;
+    }
+  }
+}
+
+template <int OP>
+__device__ __forceinline__ bool gemm_task(const Params& P, Ctx& c, Stream& st, const Task& t, int s) {
+  const int l = t.layer;
+  const int stride = P.act_stride;
+  float* rsb = c.red + 16;  // [kMaxBatch] RMSNorm scales of the sequences
+  const int kt = (int)t.nu, ch = kt < kChunkTiles ? kt : kChunkTiles, nc = kt / ch;
+  const int ks = 1 << t.kslog, upc = ch >> t.kslog;
+  const int nitems = (int)(t.a1 - t.a0) << t.kslog;
+  const int nblk = (int)(t.a1 - t.a0);
+
+  // ---- prologue: first chunk of the activation, norms, residual rows, RoPE
+  if (OP == OP_QKV || OP == OP_GU || OP == OP_LM) {
+    float rv = 0.f;
+    if (OP == OP_QKV && c.tid < P.D) rv = P.rope[(size_t)c.pos * P.D + c.tid];
+    if (OP == OP_QKV && l == 0) {
+      // embedding rows of the batch's tokens
+      __syncthreads();
+      for (int i = c.tid; i < P.B * P.H; i += kThreads) {
+        const int n = i / P.H, k = i - n * P.H;
+        const int tok = token_of(P, c, n, s, k == 0);
+        c.act[n * stride + k] = bf16_to_f32(P.embed[(size_t)tok * P.H + k]);
+      }
+      __syncthreads();
+    } else {
+      const uint64_t* src = OP == OP_GU ? P.x_attn + (size_t)l * P.H
+                                        : P.x_ffn + (size_t)(OP == OP_LM ? P.L - 1 : l - 1) * P.H;
+      if (!stage_batch(P, c, c.act, stride, src, (size_t)P.L * P.H, 0, P.H, P.H, s)) return false;
+    }
+    const float* g = OP == OP_QKV ? P.g_attn + (size_t)l * P.Hp : OP == OP_GU ? P.g_ffn + (size_t)l * P.Hp : P.g_final;
+    if (OP == OP_QKV && c.tid < P.D) c.rope[c.tid] = rv;
+    norm_batch(P, c, c.act, stride, g, rsb);
+  } else {
+    // residual rows [r0, r0 + nr) of every sequence, then the activation
+    const int r0 = (int)t.a0 * kTileRows, nr = nblk * kTileRows;
+    __syncthreads();
+    for (int i = c.tid; i < P.B * nr; i += kThreads) {
+      const int n = i / nr, k = i - n * nr;
+      float v;
+      if (OP == OP_OPROJ && l == 0) {
+        const int tok = token_of(P, c, n, s, false);
+        v = bf16_to_f32(P.embed[(size_t)tok * P.H + r0 + k]);
+      } else {
+        const uint64_t* rsrc = (OP == OP_OPROJ ? P.x_ffn + seq_off(P, n, l - 1, P.H) : P.x_attn + seq_off(P, n, l, P.H)) + r0 + k;
+        uint64_t rw = ld_tag(rsrc);
+        uint64_t t0 = 0;
+        while ((uint32_t)(rw >> 32) != c.epoch) {
+          if (poll_stop(P, t0, s, (uint32_t)(rw >> 32))) {
+            c.flags[0] = 1;
+            break;
+          }
+          rw = ld_tag(rsrc);
+        }
+        v = __uint_as_float((uint32_t)rw);
+      }
+      c.res[i] = v;
+    }
+    const uint64_t* src = OP == OP_OPROJ ? P.o + (size_t)l * P.QD : P.h + (size_t)l * P.F;
+    const int kfull = OP == OP_OPROJ ? P.QD : P.F;
+    const int kc0 = kfull < ch * kTileCols ? kfull : ch * kTileCols;
+    if (!stage_batch(P, c, c.act, stride, src, (size_t)P.L * kfull, 0, kc0, ch * kTileCols, s)) return false;
+    if (c.flags[0]) return false;
+    if (c.tid < P.B) rsb[c.tid] = 1.f;
+    __syncthreads();
+  }
+  mark(c, 1);
+
+  // ---- main loop: MFMA over the wave's tiles, chunk by chunk
+  const int n_col = c.lane & 15;
+  const bool live = n_col < P.B;
+  const int kq = (c.lane >> 4) * 8;
+  LmBestB best{-__builtin_inff(), -1};
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int cc = 0; cc < nc; ++cc) {
+    if (cc > 0) {  // next chunk of the activation (one item per wave: acc carries over)
+      const uint64_t* src = OP == OP_OPROJ ? P.o + (size_t)l * P.QD : P.h + (size_t)l * P.F;
+      const int kfull = OP == OP_OPROJ ? P.QD : P.F;
+      const int kcc = min(ch * kTileCols, kfull - cc * ch * kTileCols);
+      if (!stage_batch(P, c, c.act, stride, src, (size_t)P.L * kfull, cc * ch * kTileCols, kcc, ch * kTileCols, s))
+        return false;
+    }
+    for (int i = c.wave; i < nitems; i += kWaves) {
+      if (nc == 1) acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int col0 = (i & (ks - 1)) * upc * kTileCols;  // first column of the part inside the chunk
+      int u = 0;
+      for (; u + 4 <= upc; u += 4) {
+        uint4 v[4];
+        take4_b(P, st, c.wave, c.lane, v);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          bf16x8 hi, lo;
+          b_operand(c.act, stride, n_col, live, col0 + (u + k) * kTileCols + kq, hi, lo);
+          acc = mfma_tile(v[k], hi, lo, acc);
+        }
+      }
+      for (; u < upc; ++u) {
+        const uint4 w = take1_b(P, st, c.wave, c.lane);
+        bf16x8 hi, lo;
+        b_operand(c.act, stride, n_col, live, col0 + u * kTileCols + kq, hi, lo);
+        acc = mfma_tile(w, hi, lo, acc);
+      }
+      if (cc != nc - 1) continue;
+      const int blk = (int)t.a0 + (i >> t.kslog);
+      if (ks == 1) {
+        // lane: rows 4 * (lane / 16) + 0..3 of the block, sequence lane % 16
+        const int r = blk * kTileRows + (c.lane >> 4) * 4;
+        if (OP == OP_QKV || OP == OP_GU) {
+          if (live) {
+            epi_pair_b<OP>(P, c, l, r, n_col, acc[0], acc[1], rsb);
+            epi_pair_b<OP>(P, c, l, r + 2, n_col, acc[2], acc[3], rsb);
+          }
+        } else {
+          if (live) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) epi_row_b<OP>(P, c, t, l, r + q, n_col, acc[q], rsb, best);
+          }
+        }
+      } else {
+        float* tile = c.part + (size_t)i * (kTileRows * 16);  // [row][sequence column]
+#pragma unroll
+        for (int q = 0; q < 4; ++q) tile[((c.lane >> 4) * 4 + q) * 16 + n_col] = acc[q];
+      }
+    }
+  }
+  mark_wave(c);
+  if (ks > 1) {
+    // sum the parts of every block in part order, then the outputs
+    __syncthreads();
+    const int rows_per = (OP == OP_QKV || OP == OP_GU) ? kTileRows / 2 : kTileRows;
+    const int combos = nblk * rows_per * P.B;
+    for (int e = c.tid; e < combos; e += kThreads) {
+      const int n = e % P.B, rest = e / P.B;
+      const int j = rest / rows_per, q = rest % rows_per;
+      if (OP == OP_QKV || OP == OP_GU) {
+        float v0 = 0.f, v1 = 0.f;
+        for (int pp = 0; pp < ks; ++pp) {
+          const float* tile = c.part + (size_t)(j * ks + pp) * (kTileRows * 16);
+          v0 += tile[(2 * q) * 16 + n];
+          v1 += tile[(2 * q + 1) * 16 + n];
+        }
+        epi_pair_b<OP>(P, c, l, ((int)t.a0 + j) * kTileRows + 2 * q, n, v0, v1, rsb);
+      } else {
+        float v = 0.f;
+        for (int pp = 0; pp < ks; ++pp) v += c.part[(size_t)(j * ks + pp) * (kTileRows * 16) + q * 16 + n];
+        if (OP == OP_LM) {
+          // reduced values back into the first part's tile for the argmax scan
+          c.part[(size_t)(j * ks) * (kTileRows * 16) + q * 16 + n] = v * rsb[n];
+          P.logits[(size_t)n * P.V + ((int)t.a0 + j) * kTileRows + q] = v * rsb[n];
+        } else {
+          epi_row_b<OP>(P, c, t, l, ((int)t.a0 + j) * kTileRows + q, n, v, rsb, best);
+        }
+      }
+    }
+  }
+  mark(c, 2);
+  if (OP == OP_LM) {
+    uint64_t* keys = reinterpret_cast<uint64_t*>(c.part);
+    if (ks == 1) {
+      // lanes of one sequence column: n, n + 16, n + 32, n + 48
+      uint64_t k = live ? amax_key(best.v, best.i) : 0;
+#pragma unroll
+      for (int o = 16; o < 64; o <<= 1) {
+        const uint64_t y = __shfl_xor(k, o);
+        k = y > k ? y : k;
+      }
+      __syncthreads();
+      if (c.lane < 16) keys[c.wave * 16 + c.lane] = k;
+    } else {
+      __syncthreads();
+      // scan the reduced logits of this task (<= 8 blocks) per sequence
+      uint64_t k = 0;
+      if (c.tid < P.B) {
+        for (int j = 0; j < nblk; ++j)
+          for (int q = 0; q < kTileRows; ++q) {
+            const float v = c.part[(size_t)(j * ks) * (kTileRows * 16) + q * 16 + c.tid];
+            const uint64_t kk = amax_key(v, ((int)t.a0 + j) * kTileRows + q);
+            k = kk > k ? kk : k;
+          }
+      }
+      __syncthreads();
+      if (c.wave == 0 && c.lane < 16) keys[c.lane] = k;
+      if (c.wave > 0 && c.lane < 16) keys[c.wave * 16 + c.lane] = 0;
+    }
+    __syncthreads();
+    lm_finish_b(P, c, t);
+  }
+  return true;
+}
+
+// Batched attention: task (sequence nu, kv head a0, chunk a1); the chunk is
+// walked in blocks of kMaxChunk positions with each wave's running maximum,
+// sum and P.V rescaled from block to block.  Layout per block as in attn_task.
+template <int G, int D>
+__device__ __forceinline__ bool attn_task_b(const Params& P, Ctx& c, const Task& t, int s) {
+  constexpr int NT = D / 8;
+  constexpr int PPP = kThreads / NT;
+  constexpr int NPASS = kMaxChunk / PPP;
+  const int l = t.layer, g = (int)t.a0, ch = (int)t.a1, n = (int)t.nu;
+  const int C = P.attn_chunks;
+  const int npos = c.pos + 1;
+  const int len0 = (npos + C - 1) / C;
+  const int t0 = min(npos, ch * len0), t1 = min(npos, t0 + len0);
+
+  const size_t head_off = (seq_off(P, n, l, P.NKV) + g) * P.S * D;
+  const int ds = c.tid % NT;
+  const int pg = c.tid / NT;
+  uint4 kr[NPASS], vr[NPASS];
+  auto prefetch = [&](int base) {
+#pragma unroll
+    for (int j = 0; j < NPASS; ++j) {
+      const int tp = base + j * PPP + pg;
+      const int tl = (tp < t1 && tp != c.pos) ? tp : 0;
+      const size_t o = head_off + (size_t)tl * D + ds * 8;
+      kr[j] = *reinterpret_cast<const uint4*>(P.kcache + o);
+      vr[j] = *reinterpret_cast<const uint4*>(P.vcache + o);
+    }
+  };
+  prefetch(t0);
+
+  float* qs = c.act;
+  float* kcur = qs + G * D;
+  float* vcur = kcur + D;
+  float* wpart = vcur + D;
+  float* wm = wpart + kWaves * G * D;
+  float* wl = wm + kWaves * G;
+  {
+    const Seg seg[3] = {{qs, P.q + seq_off(P, n, l, P.QD) + (size_t)g * G * D, G * D, P.qscale},
+                        {kcur, P.kvcur + seq_off(P, n, l, 2 * P.KVD) + (size_t)g * D, D, 1.f},
+                        {vcur, P.kvcur + seq_off(P, n, l, 2 * P.KVD) + P.KVD + (size_t)g * D, D, 1.f}};
+    if (!stage_tagged(P, c, seg, s)) return false;
+  }
+  mark(c, 1);
+  float acc[G][8], ls[G], m[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    ls[h] = 0.f;
+    m[h] = -__builtin_inff();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  }
+  for (int base = t0; base < t1; base += kMaxChunk) {
+    if (base != t0) prefetch(base);
+    // this step's row (bf16-exact values staged from kvcur) into its slot
+    uint4 kb, vb;
+    {
+      const float4 k0 = *reinterpret_cast<const float4*>(kcur + ds * 8);
+      const float4 k1 = *reinterpret_cast<const float4*>(kcur + ds * 8 + 4);
+      const float4 v0 = *reinterpret_cast<const float4*>(vcur + ds * 8);
+      const float4 v1 = *reinterpret_cast<const float4*>(vcur + ds * 8 + 4);
+      kb = {pack_bf16x2(k0.x, k0.y), pack_bf16x2(k0.z, k0.w), pack_bf16x2(k1.x, k1.y), pack_bf16x2(k1.z, k1.w)};
+      vb = {pack_bf16x2(v0.x, v0.y), pack_bf16x2(v0.z, v0.w), pack_bf16x2(v1.x, v1.y), pack_bf16x2(v1.z, v1.w)};
+    }
+#pragma unroll
+    for (int j = 0; j < NPASS; ++j) {
+      const bool here = base + j * PPP + pg == c.pos;
+      kr[j].x = here ? kb.x : kr[j].x;
+      kr[j].y = here ? kb.y : kr[j].y;
+      kr[j].z = here ? kb.z : kr[j].z;
+      kr[j].w = here ? kb.w : kr[j].w;
+      vr[j].x = here ? vb.x : vr[j].x;
+      vr[j].y = here ? vb.y : vr[j].y;
+      vr[j].z = here ? vb.z : vr[j].z;
+      vr[j].w = here ? vb.w : vr[j].w;
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float4 qa = *reinterpret_cast<const float4*>(qs + h * D + ds * 8);
+      const float4 qb = *reinterpret_cast<const float4*>(qs + h * D + ds * 8 + 4);
+      float sc[NPASS];
+      float mb = -__builtin_inff();
+#pragma unroll
+      for (int j = 0; j < NPASS; ++j) {
+        const float a = slice_sum<NT>(dot8r(kr[j], qa, qb));
+        sc[j] = base + j * PPP + pg < t1 ? a : -__builtin_inff();
+        mb = fmaxf(mb, sc[j]);
+      }
+      mb = wave_max(mb);
+      const float mn = fmaxf(m[h], mb);
+      const float scale = m[h] == -__builtin_inff() ? 0.f : __expf(m[h] - mn);
+      ls[h] *= scale;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] *= scale;
+      m[h] = mn;
+#pragma unroll
+      for (int j = 0; j < NPASS; ++j) {
+        const float p = sc[j] == -__builtin_inff() ? 0.f : __expf(sc[j] - mn);
+        ls[h] += p;
+        const uint4 w = vr[j];
+        acc[h][0] = fmaf(p, bf_lo(w.x), acc[h][0]);
+        acc[h][1] = fmaf(p, bf_hi(w.x), acc[h][1]);
+        acc[h][2] = fmaf(p, bf_lo(w.y), acc[h][2]);
+        acc[h][3] = fmaf(p, bf_hi(w.y), acc[h][3]);
+        acc[h][4] = fmaf(p, bf_lo(w.z), acc[h][4]);
+        acc[h][5] = fmaf(p, bf_hi(w.z), acc[h][5]);
+        acc[h][6] = fmaf(p, bf_lo(w.w), acc[h][6]);
+        acc[h][7] = fmaf(p, bf_hi(w.w), acc[h][7]);
+      }
+    }
+  }
+  float wsum[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    wsum[h] = wave_sum(ds == 0 ? ls[h] : 0.f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = group_sum<NT>(acc[h][e]);
+  }
+  if (c.lane < NT) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float* dst = wpart + (c.wave * G + h) * D + ds * 8;
+      *reinterpret_cast<float4*>(dst) = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+    }
+  }
+  if (c.lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      wm[c.wave * G + h] = m[h];
+      wl[c.wave * G + h] = wsum[h];
+    }
+  }
+  mark_wave(c);
+  __syncthreads();
+  mark(c, 2);
+
+  const int h = c.tid / D, d = c.tid % D;
+  float A = 0.f, Ls = 0.f, M = -__builtin_inff();
+  if (c.tid < G * D) {
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wm[w * G + h]);
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = wm[w * G + h];
+      const float e = mw == -__builtin_inff() ? 0.f : __expf(mw - M);
+      A = fmaf(e, wpart[(w * G + h) * D + d], A);
+      Ls = fmaf(e, wl[w * G + h], Ls);
+    }
+  }
+  uint64_t* o = P.o + seq_off(P, n, l, P.QD) + (size_t)g * G * D;
+  if (C == 1) {
+    if (c.tid < G * D) st_tag(o + c.tid, A / Ls, c.epoch);
+    return true;
+  }
+  const int stride = G * (D + 2);
+  const size_t head = seq_off(P, n, l, P.NKV) + g;  // (sequence, layer, kv head)
+  float* mine = P.attn_part + (head * C + ch) * stride;
+  if (c.tid < G * D) st_f32_agent(mine + 2 * G + c.tid, A);
+  if (c.tid < G * D && d == 0) {
+    st_f32_agent(mine + h, M);
+    st_f32_agent(mine + G + h, Ls);
+  }
+  wait_all_vmem();
+  __syncthreads();
+  if (c.tid == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(P.attn_ctr + head, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    c.flags[1] = old == c.epoch * (uint32_t)C - 1u;
+  }
+  __syncthreads();
+  if (c.flags[1] && c.tid < G * D) {
+    const float* basep = P.attn_part + head * C * stride;
+    float MM = -__builtin_inff();
+    for (int k = 0; k < C; ++k) MM = fmaxf(MM, ld_f32_agent(basep + (size_t)k * stride + h));
+    float LL = 0.f, AA = 0.f;
+    for (int k = 0; k < C; ++k) {
+      const float* pk = basep + (size_t)k * stride;
+      const float mk = ld_f32_agent(pk + h);
+      const float e = mk == -__builtin_inff() ? 0.f : __expf(mk - MM);
+      LL = fmaf(e, ld_f32_agent(pk + G + h), LL);
+      AA = fmaf(e, ld_f32_agent(pk + 2 * G + c.tid), AA);
+    }
+    st_tag(o + c.tid, AA / LL, c.epoch);
+  }
+  return true;
+}
+
+// ---------------------------------------------------------------------------
 // the stage loop shared by the persistent kernel and the per-stage kernels
 // ---------------------------------------------------------------------------
 
 // G query heads per kv head and head_dim D are template parameters so that a
 // kernel instance carries exactly one attention variant (register budget).
-template <int G, int D>
+template <int G, int D, bool BATCHED>
 __device__ __forceinline__ void run_stages(const Params& P, int s_begin, int s_end) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   Ctx c;
@@ -1042,8 +1729,13 @@ __device__ __forceinline__ void run_stages(const Params& P, int s_begin, int s_e
   st.s_begin = s_begin;
   st.s_end = s_end;
   st.ldone = false;
-  loader_seek(P, st, s_begin, c.b, c.wave);
-  top_up(P, st, c.b, c.wave, c.lane, kRing);
+  if constexpr (BATCHED) {
+    loader_seek_b(P, st, s_begin, c.wave);
+    top_up_b(P, st, c.wave, c.lane, kRing);
+  } else {
+    loader_seek(P, st, s_begin, c.b, c.wave);
+    top_up(P, st, c.b, c.wave, c.lane, kRing);
+  }
 
   for (int s = s_begin; s < s_end; ++s) {
     const Task t = task_at(st.tape, s - s_begin);
@@ -1051,14 +1743,26 @@ __device__ __forceinline__ void run_stages(const Params& P, int s_begin, int s_e
                                                    : nullptr;
     mark(c, 0);
     bool ok = true;
-    switch (t.op) {
-      case OP_QKV: ok = gemv_task<OP_QKV>(P, c, st, t, s); break;
-      case OP_OPROJ: ok = gemv_task<OP_OPROJ>(P, c, st, t, s); break;
-      case OP_GU: ok = gemv_task<OP_GU>(P, c, st, t, s); break;
-      case OP_DOWN: ok = gemv_task<OP_DOWN>(P, c, st, t, s); break;
-      case OP_LM: ok = gemv_task<OP_LM>(P, c, st, t, s); break;
-      case OP_ATTN: ok = attn_task<G, D>(P, c, t, s); break;
-      default: break;
+    if constexpr (BATCHED) {
+      switch (t.op) {
+        case OP_QKV: ok = gemm_task<OP_QKV>(P, c, st, t, s); break;
+        case OP_OPROJ: ok = gemm_task<OP_OPROJ>(P, c, st, t, s); break;
+        case OP_GU: ok = gemm_task<OP_GU>(P, c, st, t, s); break;
+        case OP_DOWN: ok = gemm_task<OP_DOWN>(P, c, st, t, s); break;
+        case OP_LM: ok = gemm_task<OP_LM>(P, c, st, t, s); break;
+        case OP_ATTN: ok = attn_task_b<G, D>(P, c, t, s); break;
+        default: break;
+      }
+    } else {
+      switch (t.op) {
+        case OP_QKV: ok = gemv_task<OP_QKV>(P, c, st, t, s); break;
+        case OP_OPROJ: ok = gemv_task<OP_OPROJ>(P, c, st, t, s); break;
+        case OP_GU: ok = gemv_task<OP_GU>(P, c, st, t, s); break;
+        case OP_DOWN: ok = gemv_task<OP_DOWN>(P, c, st, t, s); break;
+        case OP_LM: ok = gemv_task<OP_LM>(P, c, st, t, s); break;
+        case OP_ATTN: ok = attn_task<G, D>(P, c, t, s); break;
+        default: break;
+      }
     }
     mark(c, 3);
     if (!ok) break;
@@ -1066,14 +1770,32 @@ __device__ __forceinline__ void run_stages(const Params& P, int s_begin, int s_e
   wait_all_vmem();
 }
 
-template <int G, int D>
+template <int G, int D, bool BATCHED>
 __global__ void __launch_bounds__(kThreads, 1) mk_persistent(Params P) {
-  run_stages<G, D>(P, 0, P.num_stages);
+  run_stages<G, D, BATCHED>(P, 0, P.num_stages);
 }
 
-template <int G, int D>
+template <int G, int D, bool BATCHED>
 __global__ void __launch_bounds__(kThreads, 1) mk_stage(Params P, int s) {
-  run_stages<G, D>(P, s, s + 1);
+  run_stages<G, D, BATCHED>(P, s, s + 1);
+}
+
+// Load-time repack for batched plans: source row r (< nsrc) of a bf16 matrix
+// (row stride sstride elements, kcols columns) becomes row row0 + r * rstep
+// of a tiled [rows][kp] matrix (16 x 32 tiles, 1 KiB each, in MFMA A-operand
+// lane order); columns kcols..kp-1 are zero.  One thread per 8 columns.
+__global__ void mk_tile_rows(const uint16_t* __restrict__ src, size_t sstride, int nsrc, int kcols,
+                             uint16_t* __restrict__ dst, int kp, int row0, int rstep) {
+  const int groups = kp / 8;
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (size_t)nsrc * groups) return;
+  const int r = (int)(idx / groups), k = (int)(idx % groups) * 8;
+  const int dr = row0 + r * rstep;
+  const int lane = (dr % kTileRows) + kTileRows * ((k % kTileCols) / 8);
+  const size_t tile = (size_t)(dr / kTileRows) * (kp / kTileCols) + (size_t)(k / kTileCols);
+  uint4 v = {0u, 0u, 0u, 0u};
+  if (k + 8 <= kcols) v = *reinterpret_cast<const uint4*>(src + (size_t)r * sstride + k);
+  *reinterpret_cast<uint4*>(dst + (tile * 64 + lane) * 8) = v;
 }
 
 __global__ void mk_set_args(StepArgs* a, int pos, uint32_t epoch) {
@@ -1092,44 +1814,56 @@ __global__ void mk_advance_args(StepArgs* a) {
 
 namespace {
 
-// Kernel instances for (G, D): G in {1, 2, 4}, D in {64, 128}.
+// Kernel instances: batch 1 for (G, D), G in {1, 2, 4}, D in {64, 128};
+// batched plans (head_dim 64 only) for G in {1, 2, 4}.
 struct KernelPair {
   const void* persistent;
   const void* stage;
 };
 
-template <int G, int D>
+template <int G, int D, bool BATCHED>
 KernelPair pair_of() {
-  return {reinterpret_cast<const void*>(&mk_persistent<G, D>), reinterpret_cast<const void*>(&mk_stage<G, D>)};
+  return {reinterpret_cast<const void*>(&mk_persistent<G, D, BATCHED>),
+          reinterpret_cast<const void*>(&mk_stage<G, D, BATCHED>)};
 }
 
-KernelPair kernels_for(int G, int D) {
-  if (D == 64) return G == 1 ? pair_of<1, 64>() : G == 2 ? pair_of<2, 64>() : pair_of<4, 64>();
-  return G == 1 ? pair_of<1, 128>() : G == 2 ? pair_of<2, 128>() : pair_of<4, 128>();
+KernelPair kernels_for(int G, int D, bool batched) {
+  if (batched) return G == 1 ? pair_of<1, 64, true>() : G == 2 ? pair_of<2, 64, true>() : pair_of<4, 64, true>();
+  if (D == 64) return G == 1 ? pair_of<1, 64, false>() : G == 2 ? pair_of<2, 64, false>() : pair_of<4, 64, false>();
+  return G == 1 ? pair_of<1, 128, false>() : G == 2 ? pair_of<2, 128, false>() : pair_of<4, 128, false>();
 }
 
 }  // namespace
 
-hipError_t configure_kernels(int G, int D, int lds_bytes) {
-  const KernelPair k = kernels_for(G, D);
+hipError_t configure_kernels(int G, int D, bool batched, int lds_bytes) {
+  const KernelPair k = kernels_for(G, D, batched);
   hipError_t e = hipFuncSetAttribute(k.persistent, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
   if (e != hipSuccess) return e;
   return hipFuncSetAttribute(k.stage, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
 }
 
-hipError_t persistent_occupancy(int G, int D, int lds_bytes, int* blocks_per_cu) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, kernels_for(G, D).persistent, kThreads,
+hipError_t persistent_occupancy(int G, int D, bool batched, int lds_bytes, int* blocks_per_cu) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, kernels_for(G, D, batched).persistent, kThreads,
                                                       lds_bytes);
 }
 
 hipError_t launch_persistent(const Params& P, int lds_bytes, hipStream_t stream) {
   void* args[] = {const_cast<Params*>(&P)};
-  return hipLaunchKernel(kernels_for(P.G, P.D).persistent, dim3(P.num_wgs), dim3(kThreads), args, lds_bytes, stream);
+  return hipLaunchKernel(kernels_for(P.G, P.D, P.B > 1).persistent, dim3(P.num_wgs), dim3(kThreads), args, lds_bytes, stream);
 }
 
 hipError_t launch_stage(const Params& P, int s, int lds_bytes, hipStream_t stream) {
   void* args[] = {const_cast<Params*>(&P), &s};
-  return hipLaunchKernel(kernels_for(P.G, P.D).stage, dim3(P.num_wgs), dim3(kThreads), args, lds_bytes, stream);
+  return hipLaunchKernel(kernels_for(P.G, P.D, P.B > 1).stage, dim3(P.num_wgs), dim3(kThreads), args, lds_bytes, stream);
+}
+
+hipError_t launch_tile_rows(const uint16_t* src, size_t sstride, int nsrc, int kcols, uint16_t* dst, int kp, int row0,
+                            int rstep) {
+  const size_t n = (size_t)nsrc * (kp / 8);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(mk_tile_rows, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, 0, src, sstride, nsrc, kcols, dst,
+                     kp, row0, rstep);
+  return hipGetLastError();
 }
 
 hipError_t launch_set_args(StepArgs* a, int pos, uint32_t epoch, hipStream_t stream) {

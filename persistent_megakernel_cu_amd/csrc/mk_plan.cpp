@@ -60,7 +60,12 @@ int plan_build(const mk_config& c, int W, Plan& p) {
     const int grp = c.n_heads / c.n_kv_heads;
     if (grp != 1 && grp != 2 && grp != 4) return fail(p, MK_E_UNSUPPORTED, "1, 2 or 4 query heads per kv head");
   }
-  if (c.batch != 1) return fail(p, MK_E_UNSUPPORTED, "this build decodes batch 1");
+  if (c.batch > kMaxBatch) return fail(p, MK_E_UNSUPPORTED, "at most 8 sequences per batch");
+  if (c.batch > 1) {
+    if (c.head_dim != 64) return fail(p, MK_E_UNSUPPORTED, "batched decode needs head_dim 64");
+    if (c.hidden % kTileRows != 0 || c.vocab % kTileRows != 0 || c.ffn % (kTileRows / 2) != 0)
+      return fail(p, MK_E_UNSUPPORTED, "batched decode needs hidden and vocab multiples of 16, ffn of 8");
+  }
   if (!(c.rms_eps >= 0.0f) || !(c.rope_theta > 0.0)) return fail(p, MK_E_INVAL, "rms_eps >= 0 and rope_theta > 0");
   if (c.exec_mode < MK_MODE_MEGA || c.exec_mode > MK_MODE_GRAPH) return fail(p, MK_E_INVAL, "unknown exec_mode");
   if (W <= 0 || W > 4096) return fail(p, MK_E_INVAL, "workgroup count out of range");
@@ -82,16 +87,21 @@ int plan_build(const mk_config& c, int W, Plan& p) {
   p.Hp = round_up(p.H, kRowAlign);
   p.QDp = round_up(p.QD, kRowAlign);
   p.Fp = round_up(p.F, kRowAlign);
+  p.batched = p.B > 1;
+  if (p.batched && (p.Hp > kChunkCols || p.QDp > kChunkCols))
+    return fail(p, MK_E_UNSUPPORTED, "batched decode needs hidden and n_heads * head_dim <= 2048");
 
-  // Attention split: chunks of at most kMaxChunk positions, at most one task per workgroup.
+  // Attention split: chunks of at most kMaxChunk positions (batched plans
+  // walk longer chunks in blocks), at most one task per workgroup.
+  const int seqs_kv = p.B * p.NKV;  // (sequence, kv head) pairs
   int C = c.attn_chunks;
   if (C <= 0) C = (p.S + kMaxChunk - 1) / kMaxChunk;
   C = std::max(1, std::min(C, p.S));
-  if ((int64_t)C * p.NKV > W) C = std::max(1, W / p.NKV);
-  if ((int64_t)C * p.NKV > W) return fail(p, MK_E_UNSUPPORTED, "more kv heads than workgroups");
+  if ((int64_t)C * seqs_kv > W) C = std::max(1, W / seqs_kv);
+  if ((int64_t)C * seqs_kv > W) return fail(p, MK_E_UNSUPPORTED, "more (sequence, kv head) pairs than workgroups");
   p.C = C;
   const int lmax = (p.S + C - 1) / C;  // longest chunk
-  if (lmax > kMaxChunk) return fail(p, MK_E_UNSUPPORTED, "attention chunk longer than 256 positions");
+  if (!p.batched && lmax > kMaxChunk) return fail(p, MK_E_UNSUPPORTED, "attention chunk longer than 256 positions");
 
   // ---- packed arena layout: per layer [Wq;Wk;Wv] | Wo | [gate/up interleaved] | Wd
   const uint64_t align = 4096;
@@ -111,7 +121,7 @@ int plan_build(const mk_config& c, int W, Plan& p) {
     off = round_up64(off + (uint64_t)p.H * p.Fp * 2, align);
   }
   p.arena_bytes = std::max<uint64_t>(off, align);
-  p.lm_borrowed = (p.Hp == p.H);
+  p.lm_borrowed = !p.batched && (p.Hp == p.H);  // tiled plans always repack
   p.lm_bytes = p.lm_borrowed ? 0 : (uint64_t)p.V * p.Hp * 2;
 
   // ---- tape
@@ -145,17 +155,56 @@ int plan_build(const mk_config& c, int W, Plan& p) {
       if (op == OP_OPROJ || op == OP_DOWN) max_res_rows = std::max(max_res_rows, (int)(2 * (a1 - a0)));
     }
   };
+  // Batched plans: row blocks of 16 rows over workgroups [b0, W); a task's
+  // blocks are cut into 2^kslog parts so that at least 8 (block, part) items
+  // keep the waves busy (parts split the columns of every chunk).
+  auto gemm_stage = [&](int s, Op op, int layer, uint64_t rows, uint32_t ktiles, uint64_t wofs, uint8_t region,
+                        int b0 = 0) {
+    const uint64_t blocks = rows / kTileRows;
+    const int nw = W - b0;
+    const uint32_t ch = std::min<uint32_t>(ktiles, kChunkTiles);
+    uint32_t n = 0;
+    for (int i = 0; i < nw; ++i) n += blocks * (uint64_t)(i + 1) / nw > blocks * (uint64_t)i / nw;
+    for (int i = 0; i < nw; ++i) {
+      const uint64_t a0 = blocks * (uint64_t)i / nw, a1 = blocks * (uint64_t)(i + 1) / nw;
+      if (a1 == a0) continue;
+      Task& t = p.tape[(size_t)s * W + b0 + i];
+      t.op = op;
+      t.region = region;
+      t.layer = (uint16_t)layer;
+      t.a0 = (uint32_t)a0;
+      t.a1 = (uint32_t)a1;
+      t.nu = ktiles;
+      t.wofs = wofs;
+      t.ntasks = n;
+      uint32_t k = 0;
+      while ((a1 - a0) << (k + 1) <= (uint64_t)kWaves && (ch >> (k + 1)) > 0 && ch % (2u << k) == 0) ++k;
+      t.kslog = k;
+      if (op == OP_OPROJ || op == OP_DOWN) max_res_rows = std::max(max_res_rows, (int)((a1 - a0) * kTileRows));
+    }
+  };
   for (int l = 0; l < p.L; ++l) {
     const int s0 = kStagesPerLayer * l;
-    gemv_stage(s0 + 0, OP_QKV, l, qkv_rows(p) / 2, (uint32_t)(2 * p.Hp / kUnitElems), p.off_qkv[l], 0);
-    // attention: task i = (kv head i / C, chunk i % C) on workgroup i
-    for (int i = 0; i < p.NKV * C; ++i) {
+    if (p.batched)
+      gemm_stage(s0 + 0, OP_QKV, l, qkv_rows(p), (uint32_t)(p.Hp / kTileCols), p.off_qkv[l], 0);
+    else
+      gemv_stage(s0 + 0, OP_QKV, l, qkv_rows(p) / 2, (uint32_t)(2 * p.Hp / kUnitElems), p.off_qkv[l], 0);
+    // attention: task i = (sequence, kv head, chunk) on workgroup i
+    for (int i = 0; i < seqs_kv * C; ++i) {
       Task& t = p.tape[(size_t)(s0 + 1) * W + i];
       t.op = OP_ATTN;
       t.layer = (uint16_t)l;
-      t.a0 = (uint32_t)(i / C);
+      t.nu = (uint32_t)(i / (p.NKV * C));
+      t.a0 = (uint32_t)((i / C) % p.NKV);
       t.a1 = (uint32_t)(i % C);
-      t.ntasks = (uint32_t)(p.NKV * C);
+      t.ntasks = (uint32_t)(seqs_kv * C);
+    }
+    if (p.batched) {
+      const int gu_b0 = (seqs_kv * C * 8 <= W) ? seqs_kv * C : 0;
+      gemm_stage(s0 + 2, OP_OPROJ, l, p.H, (uint32_t)(p.QDp / kTileCols), p.off_o[l], 0);
+      gemm_stage(s0 + 3, OP_GU, l, 2ull * p.F, (uint32_t)(p.Hp / kTileCols), p.off_gu[l], 0, gu_b0);
+      gemm_stage(s0 + 4, OP_DOWN, l, p.H, (uint32_t)(p.Fp / kTileCols), p.off_down[l], 0);
+      continue;
     }
     gemv_stage(s0 + 2, OP_OPROJ, l, p.H / 2, (uint32_t)(2 * p.QDp / kUnitElems), p.off_o[l], 0);
     // When attention occupies few workgroups they sit out the gate/up stage:
@@ -165,7 +214,10 @@ int plan_build(const mk_config& c, int W, Plan& p) {
     gemv_stage(s0 + 3, OP_GU, l, p.F, (uint32_t)(2 * p.Hp / kUnitElems), p.off_gu[l], 0, gu_b0);
     gemv_stage(s0 + 4, OP_DOWN, l, p.H / 2, (uint32_t)(2 * p.Fp / kUnitElems), p.off_down[l], 0);
   }
-  gemv_stage(p.stages - 1, OP_LM, p.L, p.V / 2, (uint32_t)(2 * p.Hp / kUnitElems), 0, 1);
+  if (p.batched)
+    gemm_stage(p.stages - 1, OP_LM, p.L, p.V, (uint32_t)(p.Hp / kTileCols), 0, 1);
+  else
+    gemv_stage(p.stages - 1, OP_LM, p.L, p.V / 2, (uint32_t)(2 * p.Hp / kUnitElems), 0, 1);
   p.num_tasks = 0;
   for (const Task& t : p.tape) p.num_tasks += t.op != OP_NONE;
 
@@ -173,8 +225,14 @@ int plan_build(const mk_config& c, int W, Plan& p) {
   // attention scratch: q [G][D], k and v of this step [D] each, per-wave
   // partial outputs [waves][G][D], per-wave max and sum [waves][G] each
   const int attn_floats = p.G * p.D + 2 * p.D + kWaves * p.G * p.D + 2 * kWaves * p.G;
-  p.act_floats = round_up(std::max(std::max(p.Hp, p.QDp), std::max(p.Fp, attn_floats)), 4);
-  p.res_floats = round_up(std::max(max_res_rows, 4), 4);
+  if (p.batched) {
+    p.act_stride = std::max(std::max(p.Hp, p.QDp), std::min(p.Fp, kChunkCols));
+    p.act_floats = round_up(std::max(p.B * p.act_stride, attn_floats), 4);
+    p.res_floats = round_up(std::max(p.B * max_res_rows, 4), 4);
+  } else {
+    p.act_floats = round_up(std::max(std::max(p.Hp, p.QDp), std::max(p.Fp, attn_floats)), 4);
+    p.res_floats = round_up(std::max(max_res_rows, 4), 4);
+  }
   if (max_res_rows > kThreads) return fail(p, MK_E_UNSUPPORTED, "more than 512 residual rows per workgroup");
   p.ring_units = kRing;
   p.lds_act = kRingBytes;
@@ -182,7 +240,8 @@ int plan_build(const mk_config& c, int W, Plan& p) {
   p.lds_rope = p.lds_res + p.res_floats * 4;
   p.lds_misc = p.lds_rope + round_up(p.D, 4) * 4;
   p.lds_part = p.lds_misc + 256;
-  p.lds_tape = p.lds_part + kMaxItems * 4;
+  // split-item sums; batched: one 16x16 fp32 tile per wave
+  p.lds_tape = p.lds_part + std::max(kMaxItems, kWaves * kTileRows * 16) * 4;
   p.lds_bytes = p.lds_tape + p.stages * (int)sizeof(Task);
   if (p.lds_bytes > 160 * 1024) return fail(p, MK_E_UNSUPPORTED, "LDS plan exceeds 160 KiB per workgroup");
   return MK_OK;
@@ -221,17 +280,49 @@ int plan_validate(const Plan& p, std::string* why) {
     uint32_t count = 0;
     for (int b = 0; b < W; ++b) count += p.tape[(size_t)s * W + b].op != OP_NONE;
     if (kind == OP_ATTN) {
-      std::vector<int> seen((size_t)p.NKV * p.C, 0);
+      std::vector<int> seen((size_t)p.B * p.NKV * p.C, 0);
       for (int b = 0; b < W; ++b) {
         const Task& t = p.tape[(size_t)s * W + b];
         if (t.op == OP_NONE) continue;
         if (t.op != OP_ATTN || t.layer != layer) return bad("attention stage holds another op");
-        if ((int)t.a0 >= p.NKV || (int)t.a1 >= p.C) return bad("attention task out of range");
-        if (seen[(size_t)t.a0 * p.C + t.a1]++) return bad("attention task repeated");
+        if ((int)t.a0 >= p.NKV || (int)t.a1 >= p.C || (int)t.nu >= p.B) return bad("attention task out of range");
+        if (seen[((size_t)t.nu * p.NKV + t.a0) * p.C + t.a1]++) return bad("attention task repeated");
         if (t.ntasks != count) return bad("attention task count");
       }
       for (int v : seen)
         if (v != 1) return bad("attention task missing");
+      continue;
+    }
+    if (p.batched) {
+      // GEMM: row blocks [a0, a1) must tile [0, rows / 16) exactly
+      uint64_t rows = 0, kt = 0;
+      switch (kind) {
+        case OP_QKV: rows = qkv_rows(p); kt = p.Hp / kTileCols; break;
+        case OP_OPROJ: rows = p.H; kt = p.QDp / kTileCols; break;
+        case OP_GU: rows = 2ull * p.F; kt = p.Hp / kTileCols; break;
+        case OP_DOWN: rows = p.H; kt = p.Fp / kTileCols; break;
+        default: rows = p.V; kt = p.Hp / kTileCols; break;
+      }
+      const uint64_t ch = std::min<uint64_t>(kt, kChunkTiles);
+      uint64_t next = 0;
+      for (int b = 0; b < W; ++b) {
+        const Task& t = p.tape[(size_t)s * W + b];
+        if (t.op == OP_NONE) continue;
+        if (t.op != kind || t.layer != layer) return bad("stage holds another op");
+        if (t.a0 != next || t.a1 <= t.a0) return bad("row blocks not tiled exactly");
+        next = t.a1;
+        if (t.nu != kt || t.wofs != wofs) return bad("task geometry");
+        if ((uint64_t)t.a1 * kt * kUnitBytes > region_bytes) return bad("task reads past its matrix");
+        if (t.ntasks != count) return bad("task count");
+        if (t.region != (kind == OP_LM ? 1 : 0)) return bad("weight region");
+        const uint64_t ks = 1ull << t.kslog, items = (uint64_t)(t.a1 - t.a0) * ks;
+        if (kt % ch != 0 || ch % ks != 0) return bad("parts do not divide the chunks");
+        if (ks > 1 && items > (uint64_t)kWaves) return bad("split blocks need one item per wave");
+        if (kt > ch && items > (uint64_t)kWaves) return bad("chunked rows need one item per wave");
+        if ((kind == OP_OPROJ || kind == OP_DOWN) && (uint64_t)p.B * (t.a1 - t.a0) * kTileRows > (uint64_t)p.res_floats)
+          return bad("residual rows exceed LDS");
+      }
+      if (next != rows / kTileRows) return bad("row blocks not covered");
       continue;
     }
     // GEMV: ranges must tile [0, pairs) exactly, in workgroup order

@@ -17,7 +17,8 @@ struct Plan {
   int L = 0, H = 0, Hp = 0, NQ = 0, NKV = 0, D = 0, G = 0;
   int QD = 0, QDp = 0, KVD = 0, F = 0, Fp = 0, V = 0, S = 0, B = 0;
   int W = 0;       // persistent workgroups
-  int C = 0;       // attention chunks per kv head
+  int C = 0;       // attention chunks per kv head (and sequence)
+  bool batched = false;  // B > 1: tiled weights, MFMA tasks
   int stages = 0;  // kStagesPerLayer * L + 1
   bool tied = true;
 
@@ -33,7 +34,7 @@ struct Plan {
 
   // LDS layout
   int act_floats = 0, res_floats = 0, ring_units = 0;
-  int lds_act = 0, lds_res = 0, lds_rope = 0, lds_misc = 0, lds_part = 0, lds_tape = 0, lds_bytes = 0;
+  int lds_act = 0, lds_res = 0, lds_rope = 0, lds_misc = 0, lds_part = 0, lds_tape = 0, lds_bytes = 0, act_stride = 0;
 
   std::string error;
 };

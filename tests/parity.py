@@ -149,3 +149,83 @@ def run_teacher_forced(shape, weights_np, max_seq, tokens_in, start_pos, n_steps
     finally:
         gpu.close()
     return reports
+
+
+class BatchDecoder:
+    """A batched mk Engine: B sequences share the position, each with its own cache slice."""
+
+    def __init__(self, shape, weights_np: dict, max_seq: int, batch: int, mode: str = "mega", kv_init=None, **kw):
+        import torch
+        from persistent_megakernel_cu_amd import binding as mkb
+
+        self.torch = torch
+        self.shape = shape
+        self.B = batch
+        self.wd = mkb.to_device(weights_np)
+        self.eng = mkb.Engine(shape, self.wd, max_seq, mode=mode, batch=batch, **kw)
+        dims = (batch, shape.n_layers, shape.n_kv_heads, max_seq, shape.head_dim)
+        if kv_init is None:
+            self.k = torch.zeros(dims, dtype=torch.int16, device="cuda")
+            self.v = torch.zeros(dims, dtype=torch.int16, device="cuda")
+        else:
+            self.k = torch.from_numpy(kv_init[0].view(np.int16)).cuda()
+            self.v = torch.from_numpy(kv_init[1].view(np.int16)).cuda()
+        self.logits = torch.empty((batch, shape.vocab), dtype=torch.float32, device="cuda")
+        self.out_tok = torch.empty(batch, dtype=torch.int32, device="cuda")
+        self.tok = torch.empty(batch, dtype=torch.int32, device="cuda")
+
+    def step(self, tokens, pos: int):
+        self.tok.copy_(self.torch.tensor([int(t) for t in tokens], dtype=self.torch.int32))
+        self.eng.decode_step(self.tok, pos, self.k, self.v, self.logits, self.out_tok)
+        self.torch.cuda.synchronize()
+        return self.logits.cpu().numpy().copy(), [int(x) for x in self.out_tok.cpu().tolist()]
+
+    def cache_np(self):
+        return (self.k.cpu().numpy().view(np.uint16).copy(), self.v.cpu().numpy().view(np.uint16).copy())
+
+    def close(self):
+        self.eng.close()
+
+
+def run_batched_teacher_forced(shape, weights_np, max_seq, prompts, start_pos, n_steps, mode="mega", oracle_obj=None,
+                               kv_init=None, label="", **kw):
+    """B sequences at one shared position: feed each sequence's prompt, then the
+    oracle's greedy tokens; every step checks every sequence against its own
+    oracle cache (logit tolerance, out_token == own argmax, cache slots)."""
+    o = oracle_obj or orc.Oracle(shape, weights_np)
+    B = len(prompts)
+    if kv_init is None:
+        caches = [o.new_cache(max_seq) for _ in range(B)]
+    else:
+        caches = [(kv_init[0][n].copy(), kv_init[1][n].copy()) for n in range(B)]
+    gpu = BatchDecoder(shape, weights_np, max_seq, B, mode=mode, kv_init=kv_init, **kw)
+    worst = 0.0
+    mism = 0
+    try:
+        seqs = [list(p) for p in prompts]
+        plen = len(seqs[0])
+        pos = start_pos
+        for i in range(plen + n_steps):
+            toks = [s[i] for s in seqs]
+            before = gpu.cache_np()
+            lg, outs = gpu.step(toks, pos)
+            after = gpu.cache_np()
+            for n in range(B):
+                kc, vc = caches[n]
+                lg_ref = o.decode_step(int(toks[n]), pos, kc, vc)
+                rep = check_step(pos, lg[n], outs[n], lg_ref, (before[0][n], before[1][n]),
+                                 (after[0][n], after[1][n]), (kc, vc))
+                worst = max(worst, rep.max_abs_err / rep.tol)
+                if i >= plen - 1:
+                    if rep.gpu_token != rep.oracle_token:
+                        assert rep.margin < rep.tol, (f"seq {n} pos {pos}: greedy token {rep.gpu_token} != oracle "
+                                                      f"{rep.oracle_token} with margin {rep.margin:.4g}")
+                        mism += 1
+                    if i >= plen - 1 and len(seqs[n]) <= i + 1:
+                        seqs[n].append(rep.oracle_token)
+            pos += 1
+        log(f"[parity] {label} mode={mode} batch={B} steps={plen + n_steps} worst err/tol={worst:.3g} "
+            f"token mismatches (all below margin)={mism}")
+    finally:
+        gpu.close()
+    return worst

@@ -6,7 +6,7 @@ import pytest
 
 import oracle as orc
 from synth_inputs import LLAMA_1B, TINY, make_kv_cache, make_prompt, make_start_token, make_weights
-from tests.parity import GpuDecoder, log, logit_tol, run_teacher_forced
+from tests.parity import GpuDecoder, log, logit_tol, run_batched_teacher_forced, run_teacher_forced
 
 pytestmark = pytest.mark.gpu
 
@@ -197,3 +197,29 @@ def test_llama8b_shape_refused():
     with pytest.raises(mkb.MkError) as e:
         mkb.Engine(LLAMA_8B, w, 2112)
     assert e.value.code == mkb.MK_E_UNSUPPORTED
+
+
+@pytest.mark.parametrize("mode", ["mega", "multi", "graph"])
+def test_tiny_batched(tiny_w, mode):
+    # 4 sequences with their own prompts, tiled weights and MFMA
+    prompts = [make_prompt(TINY, 6, master=10 + n) for n in range(4)]
+    run_batched_teacher_forced(TINY, tiny_w, 48, prompts, 0, 6, mode=mode, label="tiny-b4")
+
+
+def test_tiny_batched_untied_chunked():
+    # untied LM head, 3 sequences, attention split in 4 chunks per (sequence, kv head)
+    sh = TINY.with_(tie_embeddings=False)
+    w = make_weights(sh, master=4, gain_jitter=0.1)
+    prompts = [make_prompt(sh, 5, master=20 + n) for n in range(3)]
+    run_batched_teacher_forced(sh, w, 48, prompts, 0, 4, mode="mega", attn_chunks=4, label="tiny-b3-untied")
+
+
+def test_llama1b_batch8_seeded_cache(llama1b):
+    # batch 8 over seeded 1024-slot caches (attention chunks walked in blocks): two steps
+    from synth_inputs import make_start_token
+
+    w, o = llama1b
+    kv = make_kv_cache(LLAMA_1B, 8, 1088, 1024, master=0)
+    starts = [[make_start_token(LLAMA_1B, n)] for n in range(8)]
+    run_batched_teacher_forced(LLAMA_1B, w, 1088, starts, 1024, 1, mode="mega", oracle_obj=o, kv_init=kv,
+                               label="llama1b-b8")

@@ -39,6 +39,19 @@ def test_plan_validates(shape, max_seq, chunks):
         assert info.weight_bytes <= shape.n_layers * per_layer + 5 * shape.n_layers * 4096
 
 
+@pytest.mark.parametrize("shape,max_seq,batch,chunks", [
+    (TINY, 48, 4, 1), (TINY, 48, 8, 1), (LLAMA_1B, 1088, 8, 4), (LLAMA_1B, 256, 2, 1)])
+def test_plan_batched_validates(shape, max_seq, batch, chunks):
+    # tiled plans: every (sequence, kv head, chunk) has a task, the LM head is repacked
+    info = mkb.plan_describe(shape, max_seq, 256, batch=batch)
+    assert info.attn_chunks == chunks
+    assert info.num_stages == 5 * shape.n_layers + 1
+    assert info.lds_bytes <= 160 * 1024
+    H, QD, KVD, F, V = shape.hidden, shape.q_dim, shape.kv_dim, shape.ffn, shape.vocab
+    per_layer = 2 * (QD * H + 2 * KVD * H + H * QD + 2 * F * H + H * F)
+    assert info.weight_bytes >= shape.n_layers * per_layer + 2 * V * H
+
+
 @pytest.mark.parametrize("wgs", [2, 7, 64, 255, 256])
 def test_plan_any_workgroup_count(wgs):
     info = mkb.plan_describe(TINY, 48, wgs)
@@ -62,9 +75,11 @@ def test_plan_rejects_bad_configs():
         sh = TINY.with_(**kw)
         with pytest.raises(mkb.MkError):
             mkb.plan_describe(sh, 48, 256)
-    with pytest.raises(mkb.MkError) as e:
-        mkb.plan_describe(TINY, 48, 256, batch=2)
-    assert e.value.code == mkb.MK_E_UNSUPPORTED
+    for kw in (dict(batch=9), dict(batch=2, head_dim=128)):  # batches of 2..8, head_dim 64
+        sh = TINY.with_(**{k: v for k, v in kw.items() if k != "batch"})
+        with pytest.raises(mkb.MkError) as e:
+            mkb.plan_describe(sh, 48, 256, batch=kw["batch"])
+        assert e.value.code == mkb.MK_E_UNSUPPORTED
     c = mkb.make_config(TINY, 48)
     info = mkb.MkPlanInfo()
     assert mkb.lib().mk_plan_describe(None, 256, ctypes.byref(info)) == mkb.MK_E_INVAL
