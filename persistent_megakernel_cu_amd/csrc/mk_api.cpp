@@ -45,12 +45,12 @@ Workspace layout_workspace(const Plan& p) {
   Workspace w{};
   size_t cur = 0;
   const size_t L = std::max(p.L, 1), B = p.B;
-  w.x_attn = take(cur, B * L * p.H * 8);
-  w.x_ffn = take(cur, B * L * p.H * 8);
-  w.q = take(cur, B * L * p.QD * 8);
-  w.kvcur = take(cur, B * L * 2 * p.KVD * 8);
-  w.o = take(cur, B * L * p.QD * 8);
-  w.h = take(cur, B * L * p.F * 8);
+  w.x_attn = take(cur, B * L * p.H * 4);
+  w.x_ffn = take(cur, B * L * p.H * 4);
+  w.q = take(cur, B * L * p.QD * 4);
+  w.kvcur = take(cur, B * L * 2 * p.KVD * 4);
+  w.o = take(cur, B * L * p.QD * 4);
+  w.h = take(cur, B * L * p.F * 4);
   w.attn_part = take(cur, B * L * p.NKV * p.C * p.G * (p.D + 2) * 4);
   w.attn_ctr = take(cur, B * L * p.NKV * 4);
   w.amax = take(cur, B * p.W * 8);
@@ -133,12 +133,12 @@ Params make_params(mk_handle* h) {
   P.rope = h->rope;
   char* ws = h->ws;
   const Workspace& w = h->wl;
-  P.x_attn = reinterpret_cast<uint64_t*>(ws + w.x_attn);
-  P.x_ffn = reinterpret_cast<uint64_t*>(ws + w.x_ffn);
-  P.q = reinterpret_cast<uint64_t*>(ws + w.q);
-  P.kvcur = reinterpret_cast<uint64_t*>(ws + w.kvcur);
-  P.o = reinterpret_cast<uint64_t*>(ws + w.o);
-  P.h = reinterpret_cast<uint64_t*>(ws + w.h);
+  P.x_attn = reinterpret_cast<uint32_t*>(ws + w.x_attn);
+  P.x_ffn = reinterpret_cast<uint32_t*>(ws + w.x_ffn);
+  P.q = reinterpret_cast<uint32_t*>(ws + w.q);
+  P.kvcur = reinterpret_cast<uint32_t*>(ws + w.kvcur);
+  P.o = reinterpret_cast<uint32_t*>(ws + w.o);
+  P.h = reinterpret_cast<uint32_t*>(ws + w.h);
   P.attn_part = reinterpret_cast<float*>(ws + w.attn_part);
   P.attn_ctr = reinterpret_cast<uint32_t*>(ws + w.attn_ctr);
   P.amax = reinterpret_cast<uint64_t*>(ws + w.amax);

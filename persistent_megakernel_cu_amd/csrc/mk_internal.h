@@ -116,13 +116,14 @@ struct Params {
   const float* g_final;  // [Hp]
   const float* rope;     // [S][D/2][2] cos, sin
 
-  // tagged activations: {fp32 value, epoch tag} per element
-  uint64_t* x_attn;      // [B][L][H]   residual after attention
-  uint64_t* x_ffn;       // [B][L][H]   residual after FFN
-  uint64_t* q;           // [B][L][QD]  rotated queries
-  uint64_t* kvcur;       // [B][L][2][KVD] this step's bf16-rounded k, v
-  uint64_t* o;           // [B][L][QD]  attention output
-  uint64_t* h;           // [B][L][F]   SwiGLU hidden
+  // tagged activations: one 32-bit word per element, the fp32 value's 24
+  // high bits and the step's tag (epoch mod 256) in the low byte
+  uint32_t* x_attn;      // [B][L][H]   residual after attention
+  uint32_t* x_ffn;       // [B][L][H]   residual after FFN
+  uint32_t* q;           // [B][L][QD]  rotated queries
+  uint32_t* kvcur;       // [B][L][2][KVD] this step's bf16-rounded k, v
+  uint32_t* o;           // [B][L][QD]  attention output
+  uint32_t* h;           // [B][L][F]   SwiGLU hidden
   float* attn_part;      // [B][L][NKV][C][G*(D+2)] split-KV partials
   uint32_t* attn_ctr;    // [B][L][NKV] merge counters (epoch * C per step)
   uint64_t* amax;        // [B][num_wgs] argmax keys

@@ -83,11 +83,42 @@ __device__ __forceinline__ void lds_read4(uint4 (&v)[4], const uint32_t (&a)[4])
       : "memory");
 }
 
-__device__ __forceinline__ void st_tag(uint64_t* p, float v, uint32_t tag) {
-  __hip_atomic_store(p, ((uint64_t)tag << 32) | (uint64_t)__float_as_uint(v), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
+// Tagged activation word: an fp32 value rounded to 24 high bits (relative
+// error <= 2^-16) whose low byte carries the step's tag (epoch mod 256).  A
+// 4-byte store is single-copy atomic, so a reader that sees this step's tag
+// sees this step's value; every buffer is rewritten on every step, so the
+// previous step's tag (epoch - 1) never matches.  Readers clear the tag bits,
+// so values do not depend on the epoch.
+typedef uint32_t tword;
+__device__ __forceinline__ void st_tag(tword* p, float v, uint32_t epoch) {
+  const uint32_t w = ((__float_as_uint(v) + 0x80u) & 0xFFFFFF00u) | (epoch & 0xFFu);
+  __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint64_t ld_tag(const uint64_t* p) {
+__device__ __forceinline__ tword ld_tag(const tword* p) {
+  return __hip_atomic_load(const_cast<tword*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool tag_ready(tword w, uint32_t epoch) { return ((w ^ epoch) & 0xFFu) == 0; }
+__device__ __forceinline__ uint32_t tag_of(tword w) { return w & 0xFFu; }
+__device__ __forceinline__ float tag_value(tword w) { return __uint_as_float(w & 0xFFFFFF00u); }
+// A word that is ready with value v_bits (low byte zero), for elements that need no wait.
+__device__ __forceinline__ tword ready_word(uint32_t epoch, uint32_t v_bits = 0u) { return v_bits | (epoch & 0xFFu); }
+// Four consecutive tagged words (16-byte aligned) in one coherent load; each
+// word is checked on its own, so a load that sees some new and some old words
+// is simply polled again.
+typedef uint32_t tword4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const volatile tword4 gtword4;
+__device__ __forceinline__ tword4 ld_tag4(const tword* p) { return *(gtword4*)p; }
+__device__ __forceinline__ bool tag4_ready(tword4 w, uint32_t epoch) {
+  return ((((w.x ^ epoch) | (w.y ^ epoch) | (w.z ^ epoch) | (w.w ^ epoch)) & 0xFFu) == 0);
+}
+__device__ __forceinline__ tword4 ready_word4(uint32_t epoch) {
+  const tword r = ready_word(epoch);
+  return tword4{r, r, r, r};
+}
+__device__ __forceinline__ float4 tag_value4(tword4 w) {
+  return make_float4(tag_value(w.x), tag_value(w.y), tag_value(w.z), tag_value(w.w));
+}
+__device__ __forceinline__ uint64_t ld_u64_agent(const uint64_t* p) {
   return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void st_f32_agent(float* p, float v) {
@@ -239,22 +270,21 @@ __device__ __forceinline__ bool poll_stop(const Params& P, uint64_t& t0, int sta
 // A run of tagged elements to stage into LDS: dst[i] = value(src[i]) * scale.
 struct Seg {
   float* dst;
-  const uint64_t* src;
+  const tword* src;
   int n;
   float scale;
 };
 
-constexpr int kStageLoads = 8;  // tagged loads per thread issued in one round
+// 16-byte loads (4 tagged words) per thread issued in one staging round:
+// 8192 words per round for one sequence, 16384 for a batch.
+constexpr int kStageLoads = 4;
+constexpr int kStageLoadsBatch = 8;
 
-// Copy tagged segments into LDS as fp32 once every element carries this
-// step's tag, and zero zdst[zfrom, zto).  WG-cooperative.  All loads of a
-// round are issued before any is checked, and the first round's loads are in
-// flight before the barrier that separates these LDS writes from the previous
-// task's last LDS reads.  Ends with a barrier; false if the wait was aborted.
-// Source element of flat index i over the segments (null past the end).
+// Source of the 4-word group starting at flat index i over the segments
+// (null past the end).  Segment lengths are multiples of 4.
 template <int NSEG>
-__device__ __forceinline__ const uint64_t* seg_src(const Seg (&seg)[NSEG], int i) {
-  const uint64_t* r = nullptr;
+__device__ __forceinline__ const tword* seg_src(const Seg (&seg)[NSEG], int i) {
+  const tword* r = nullptr;
 #pragma unroll
   for (int k = 0; k < NSEG; ++k) {
     if (i >= 0 && i < seg[k].n) r = seg[k].src + i;
@@ -263,16 +293,25 @@ __device__ __forceinline__ const uint64_t* seg_src(const Seg (&seg)[NSEG], int i
   return r;
 }
 
-// Store the value of flat index i into its segment's LDS destination.
+// Store the group of 4 values starting at flat index i into its segment's LDS destination.
 template <int NSEG>
-__device__ __forceinline__ void seg_store(const Seg (&seg)[NSEG], int i, uint64_t w) {
+__device__ __forceinline__ void seg_store(const Seg (&seg)[NSEG], int i, tword4 w) {
 #pragma unroll
   for (int k = 0; k < NSEG; ++k) {
-    if (i >= 0 && i < seg[k].n) seg[k].dst[i] = __uint_as_float((uint32_t)w) * seg[k].scale;
+    if (i >= 0 && i < seg[k].n) {
+      const float4 v = tag_value4(w);
+      const float sc = seg[k].scale;
+      *reinterpret_cast<float4*>(seg[k].dst + i) = make_float4(v.x * sc, v.y * sc, v.z * sc, v.w * sc);
+    }
     i -= seg[k].n;
   }
 }
 
+// Copy tagged segments into LDS as fp32 once every element carries this
+// step's tag, and zero zdst[zfrom, zto).  WG-cooperative.  All loads of a
+// round are issued before any is checked, and the first round's loads are in
+// flight before the barrier that separates these LDS writes from the previous
+// task's last LDS reads.  Ends with a barrier; false if the wait was aborted.
 template <int NSEG, int NL = kStageLoads>
 __device__ __forceinline__ bool stage_tagged(const Params& P, Ctx& c, const Seg (&seg)[NSEG], int stage,
                                              float* zdst = nullptr, int zfrom = 0, int zto = 0) {
@@ -280,28 +319,28 @@ __device__ __forceinline__ bool stage_tagged(const Params& P, Ctx& c, const Seg 
 #pragma unroll
   for (int k = 0; k < NSEG; ++k) total += seg[k].n;
   bool stop = false;
-  for (int i0 = 0; i0 == 0 || i0 < total; i0 += kThreads * NL) {
-    uint64_t w[NL];
+  for (int i0 = 0; i0 == 0 || i0 < total; i0 += 4 * kThreads * NL) {
+    tword4 w[NL];
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
-      const uint64_t* p = seg_src(seg, i0 + j * kThreads + c.tid);
-      w[j] = p ? ld_tag(p) : ((uint64_t)c.epoch << 32);
+      const tword* p = seg_src(seg, i0 + 4 * (j * kThreads + c.tid));
+      w[j] = p ? ld_tag4(p) : ready_word4(c.epoch);
     }
     uint64_t t0 = 0;
     while (!stop) {
       bool ready = true;
 #pragma unroll
-      for (int j = 0; j < NL; ++j) ready &= (uint32_t)(w[j] >> 32) == c.epoch;
+      for (int j = 0; j < NL; ++j) ready &= tag4_ready(w[j], c.epoch);
       if (ready) break;
-      if (poll_stop(P, t0, stage, (uint32_t)(w[0] >> 32))) {
+      if (poll_stop(P, t0, stage, tag_of(w[0].x))) {
         stop = true;
         break;
       }
 #pragma unroll
       for (int j = 0; j < NL; ++j) {
-        if ((uint32_t)(w[j] >> 32) != c.epoch) {
-          const uint64_t* p = seg_src(seg, i0 + j * kThreads + c.tid);
-          if (p) w[j] = ld_tag(p);
+        if (!tag4_ready(w[j], c.epoch)) {
+          const tword* p = seg_src(seg, i0 + 4 * (j * kThreads + c.tid));
+          if (p) w[j] = ld_tag4(p);
         }
       }
     }
@@ -310,7 +349,7 @@ __device__ __forceinline__ bool stage_tagged(const Params& P, Ctx& c, const Seg 
       for (int i = zfrom + c.tid; i < zto; i += kThreads) zdst[i] = 0.f;
     }
 #pragma unroll
-    for (int j = 0; j < NL; ++j) seg_store(seg, i0 + j * kThreads + c.tid, w[j]);
+    for (int j = 0; j < NL; ++j) seg_store(seg, i0 + 4 * (j * kThreads + c.tid), w[j]);
   }
   if (stop) c.flags[0] = 1;
   __syncthreads();
@@ -335,7 +374,7 @@ __device__ __forceinline__ float block_sum(Ctx& c, float v) {
 // first layer, the bf16 embedding row of the input token (src == null).  The
 // sum of squares is reduced under the barrier that ends the staging.
 // WG-cooperative; false if the wait was aborted.
-__device__ __forceinline__ bool stage_normed(const Params& P, Ctx& c, float* dst, const uint64_t* src, const float* g,
+__device__ __forceinline__ bool stage_normed(const Params& P, Ctx& c, float* dst, const tword* src, const float* g,
                                              int n, int npad, int stage) {
   const uint16_t* emb = nullptr;
   if (src == nullptr) {
@@ -351,45 +390,48 @@ __device__ __forceinline__ bool stage_normed(const Params& P, Ctx& c, float* dst
     __syncthreads();
     emb = P.embed + (size_t)c.flags[2] * P.H;
   }
-  const uint64_t ready_tag = (uint64_t)c.epoch << 32;
+  // groups of 4 elements (n is a multiple of 4): one 16-byte load each
   float ss = 0.f;
   bool stop = false;
-  for (int i0 = 0; i0 == 0 || i0 < n; i0 += kThreads * kStageLoads) {
-    uint64_t w[kStageLoads];
-    float gv[kStageLoads];
+  for (int i0 = 0; i0 == 0 || i0 < n; i0 += 4 * kThreads * kStageLoads) {
+    tword4 w[kStageLoads];
+    float4 gv[kStageLoads];
     if (emb) {
       // in-bounds loads for every lane first (clamped index), then widen
-      uint32_t e16[kStageLoads];
+      uint2 e16[kStageLoads];
 #pragma unroll
       for (int j = 0; j < kStageLoads; ++j) {
-        const int i = i0 + j * kThreads + c.tid;
-        gv[j] = g[i < n ? i : n - 1];
-        e16[j] = emb[i < n ? i : n - 1];
+        const int i = i0 + 4 * (j * kThreads + c.tid);
+        const int ic = i < n ? i : n - 4;
+        gv[j] = *reinterpret_cast<const float4*>(g + ic);
+        e16[j] = *reinterpret_cast<const uint2*>(emb + ic);
       }
 #pragma unroll
-      for (int j = 0; j < kStageLoads; ++j) w[j] = ready_tag | (uint64_t)(e16[j] << 16);
+      for (int j = 0; j < kStageLoads; ++j)
+        w[j] = tword4{ready_word(c.epoch, e16[j].x << 16), ready_word(c.epoch, e16[j].x & 0xFFFF0000u),
+                      ready_word(c.epoch, e16[j].y << 16), ready_word(c.epoch, e16[j].y & 0xFFFF0000u)};
     } else {
 #pragma unroll
       for (int j = 0; j < kStageLoads; ++j) {
-        const int i = i0 + j * kThreads + c.tid;
-        gv[j] = g[i < n ? i : n - 1];
-        w[j] = i < n ? ld_tag(src + i) : ready_tag;
+        const int i = i0 + 4 * (j * kThreads + c.tid);
+        gv[j] = *reinterpret_cast<const float4*>(g + (i < n ? i : n - 4));
+        w[j] = i < n ? ld_tag4(src + i) : ready_word4(c.epoch);
       }
     }
     uint64_t t0 = 0;
     while (!stop) {
       bool ready = true;
 #pragma unroll
-      for (int j = 0; j < kStageLoads; ++j) ready &= (uint32_t)(w[j] >> 32) == c.epoch;
+      for (int j = 0; j < kStageLoads; ++j) ready &= tag4_ready(w[j], c.epoch);
       if (ready) break;
-      if (poll_stop(P, t0, stage, (uint32_t)(w[0] >> 32))) {
+      if (poll_stop(P, t0, stage, tag_of(w[0].x))) {
         stop = true;
         break;
       }
 #pragma unroll
       for (int j = 0; j < kStageLoads; ++j) {
-        const int i = i0 + j * kThreads + c.tid;
-        if (i < n && (uint32_t)(w[j] >> 32) != c.epoch) w[j] = ld_tag(src + i);
+        const int i = i0 + 4 * (j * kThreads + c.tid);
+        if (i < n && !tag4_ready(w[j], c.epoch)) w[j] = ld_tag4(src + i);
       }
     }
     if (i0 == 0) {
@@ -398,11 +440,15 @@ __device__ __forceinline__ bool stage_normed(const Params& P, Ctx& c, float* dst
     }
 #pragma unroll
     for (int j = 0; j < kStageLoads; ++j) {
-      const int i = i0 + j * kThreads + c.tid;
+      const int i = i0 + 4 * (j * kThreads + c.tid);
       if (i < n) {
-        const float x = __uint_as_float((uint32_t)w[j]);
-        ss = fmaf(x, x, ss);
-        dst[i] = x * gv[j];
+        const float4 x = tag_value4(w[j]);
+        ss = fmaf(x.x, x.x, ss);
+        ss = fmaf(x.y, x.y, ss);
+        ss = fmaf(x.z, x.z, ss);
+        ss = fmaf(x.w, x.w, ss);
+        *reinterpret_cast<float4*>(dst + i) =
+            make_float4(x.x * gv[j].x, x.y * gv[j].y, x.z * gv[j].z, x.w * gv[j].w);
       }
     }
   }
@@ -556,7 +602,7 @@ __device__ __forceinline__ float dot_units(const Params& P, Stream& st, Ctx& c, 
 // ---------------------------------------------------------------------------
 
 // Residual input of layer l >= 1 (x after the previous layer).
-__device__ __forceinline__ const uint64_t* x_in(const Params& P, int l) {
+__device__ __forceinline__ const tword* x_in(const Params& P, int l) {
   return P.x_ffn + (size_t)(l - 1) * P.H;
 }
 
@@ -579,37 +625,33 @@ __device__ __forceinline__ bool gemv_prologue(const Params& P, Ctx& c, const Tas
   } else {  // OPROJ, DOWN: plain activation + residual rows of this task
     const int n = OP == OP_OPROJ ? P.QD : P.F;
     const int np = OP == OP_OPROJ ? P.QDp : P.Fp;
-    const uint64_t* src = OP == OP_OPROJ ? P.o + (size_t)l * P.QD : P.h + (size_t)l * P.F;
+    const tword* src = OP == OP_OPROJ ? P.o + (size_t)l * P.QD : P.h + (size_t)l * P.F;
     const int r0 = 2 * (int)t.a0, nr = 2 * (int)(t.a1 - t.a0);
     // The residual rows were produced at least two stages earlier: read them
     // into registers before waiting for the activation (nr <= 512 rows).
-    const uint64_t* rs = OP == OP_OPROJ ? (l == 0 ? nullptr : x_in(P, l) + r0) : P.x_attn + (size_t)l * P.H + r0;
-    uint64_t rw = (uint64_t)c.epoch << 32;
+    const tword* rs = OP == OP_OPROJ ? (l == 0 ? nullptr : x_in(P, l) + r0) : P.x_attn + (size_t)l * P.H + r0;
+    tword rw = ready_word(c.epoch);
     if (c.tid < nr) {
       if (rs) {
         rw = ld_tag(rs + c.tid);
       } else {  // layer 0: the residual is the embedding row itself
         int tok = P.token[0];
         tok = (tok < 0 || tok >= P.V) ? 0 : tok;
-        rw |= (uint64_t)((uint32_t)P.embed[(size_t)tok * P.H + r0 + c.tid] << 16);
+        rw |= (uint32_t)P.embed[(size_t)tok * P.H + r0 + c.tid] << 16;
       }
     }
     const Seg seg[1] = {{c.act, src, n, 1.f}};
-    if (OP == OP_DOWN) {
-      if (!stage_tagged<1, 2 * kStageLoads>(P, c, seg, s, c.act, n, np)) return false;
-    } else {
-      if (!stage_tagged(P, c, seg, s, c.act, n, np)) return false;
-    }
+    if (!stage_tagged(P, c, seg, s, c.act, n, np)) return false;
     if (c.tid < nr) {
       uint64_t t0 = 0;
-      while ((uint32_t)(rw >> 32) != c.epoch) {
-        if (poll_stop(P, t0, s, (uint32_t)(rw >> 32))) {
+      while (!tag_ready(rw, c.epoch)) {
+        if (poll_stop(P, t0, s, tag_of(rw))) {
           c.flags[0] = 1;
           break;
         }
         rw = ld_tag(rs + c.tid);
       }
-      c.res[c.tid] = __uint_as_float((uint32_t)rw);
+      c.res[c.tid] = tag_value(rw);
     }
     __syncthreads();
     if (c.flags[0]) return false;
@@ -666,7 +708,7 @@ __device__ __forceinline__ void gemv_epilogue(const Params& P, Ctx& c, const Tas
       if (w1) st_tag(P.kvcur + ((size_t)l * 2 + 1) * P.KVD + rr + 1, bf16_to_f32(b1), tag);
     }
   } else if (OP == OP_OPROJ || OP == OP_DOWN) {
-    uint64_t* dst = (OP == OP_OPROJ ? P.x_attn : P.x_ffn) + (size_t)l * P.H + r;
+    tword* dst = (OP == OP_OPROJ ? P.x_attn : P.x_ffn) + (size_t)l * P.H + r;
     const int k = r - 2 * (int)t.a0;
     if (w0) st_tag(dst, c.res[k] + v0, tag);
     if (w1) st_tag(dst + 1, c.res[k + 1] + v1, tag);
@@ -701,7 +743,7 @@ __device__ __forceinline__ void lm_finish(const Params& P, Ctx& c, const Task& t
   if (c.flags[1] && c.wave == 0) {
     uint64_t k = 0;
     for (int w = c.lane; w < P.num_wgs; w += 64) {
-      const uint64_t x = ld_tag(P.amax + w);
+      const uint64_t x = ld_u64_agent(P.amax + w);
       k = x > k ? x : k;
     }
 #pragma unroll
@@ -957,7 +999,7 @@ __device__ __forceinline__ bool attn_task(const Params& P, Ctx& c, const Task& t
       Ls = fmaf(e, wl[w * G + h], Ls);
     }
   }
-  uint64_t* o = P.o + (size_t)l * P.QD + (size_t)g * G * D;
+  tword* o = P.o + (size_t)l * P.QD + (size_t)g * G * D;
   if (C == 1) {
     if (c.tid < G * D) st_tag(o + c.tid, A / Ls, c.epoch);
     return true;
@@ -1094,34 +1136,35 @@ __device__ __forceinline__ uint4 take1_b(const Params& P, Stream& st, int wave, 
 // dst[n * stride + k] = src_n[k0 + k], src_n = base + n * sstride.  The first
 // round's loads are in flight before the barrier that separates these LDS
 // writes from the previous task's reads.  Ends with a barrier.
-__device__ __forceinline__ bool stage_batch(const Params& P, Ctx& c, float* dst, int stride, const uint64_t* base,
+__device__ __forceinline__ bool stage_batch(const Params& P, Ctx& c, float* dst, int stride, const tword* base,
                                             size_t sstride, int k0, int kc, int kpad, int stage) {
+  // groups of 4 columns (kc, k0, sstride and stride are multiples of 4)
   const int total = P.B * kc;
   bool stop = false;
-  for (int i0 = 0; i0 == 0 || i0 < total; i0 += kThreads * kStageLoads) {
-    uint64_t w[kStageLoads];
+  for (int i0 = 0; i0 == 0 || i0 < total; i0 += 4 * kThreads * kStageLoadsBatch) {
+    tword4 w[kStageLoadsBatch];
 #pragma unroll
-    for (int j = 0; j < kStageLoads; ++j) {
-      const int i = i0 + j * kThreads + c.tid;
+    for (int j = 0; j < kStageLoadsBatch; ++j) {
+      const int i = i0 + 4 * (j * kThreads + c.tid);
       const int n = i < total ? i / kc : 0, k = i - n * kc;
-      w[j] = i < total ? ld_tag(base + (size_t)n * sstride + k0 + k) : ((uint64_t)c.epoch << 32);
+      w[j] = i < total ? ld_tag4(base + (size_t)n * sstride + k0 + k) : ready_word4(c.epoch);
     }
     uint64_t t0 = 0;
     while (!stop) {
       bool ready = true;
 #pragma unroll
-      for (int j = 0; j < kStageLoads; ++j) ready &= (uint32_t)(w[j] >> 32) == c.epoch;
+      for (int j = 0; j < kStageLoadsBatch; ++j) ready &= tag4_ready(w[j], c.epoch);
       if (ready) break;
-      if (poll_stop(P, t0, stage, (uint32_t)(w[0] >> 32))) {
+      if (poll_stop(P, t0, stage, tag_of(w[0].x))) {
         stop = true;
         break;
       }
 #pragma unroll
-      for (int j = 0; j < kStageLoads; ++j) {
-        const int i = i0 + j * kThreads + c.tid;
-        if (i < total && (uint32_t)(w[j] >> 32) != c.epoch) {
+      for (int j = 0; j < kStageLoadsBatch; ++j) {
+        const int i = i0 + 4 * (j * kThreads + c.tid);
+        if (i < total && !tag4_ready(w[j], c.epoch)) {
           const int n = i / kc, k = i - n * kc;
-          w[j] = ld_tag(base + (size_t)n * sstride + k0 + k);
+          w[j] = ld_tag4(base + (size_t)n * sstride + k0 + k);
         }
       }
     }
@@ -1132,11 +1175,11 @@ __device__ __forceinline__ bool stage_batch(const Params& P, Ctx& c, float* dst,
       for (int i = c.tid; i < P.B * padw; i += kThreads) dst[(i / padw) * stride + kc + i % padw] = 0.f;
     }
 #pragma unroll
-    for (int j = 0; j < kStageLoads; ++j) {
-      const int i = i0 + j * kThreads + c.tid;
+    for (int j = 0; j < kStageLoadsBatch; ++j) {
+      const int i = i0 + 4 * (j * kThreads + c.tid);
       if (i < total) {
         const int n = i / kc, k = i - n * kc;
-        dst[n * stride + k] = __uint_as_float((uint32_t)w[j]);
+        *reinterpret_cast<float4*>(dst + n * stride + k) = tag_value4(w[j]);
       }
     }
   }
@@ -1223,7 +1266,7 @@ __device__ __forceinline__ void epi_pair_b(const Params& P, const Ctx& c, int l,
       const float y0 = v0 * cs - v1 * sn;
       const float y1 = v0 * sn + v1 * cs;
       if (r < P.QD) {
-        uint64_t* q = P.q + seq_off(P, n, l, P.QD) + r;
+        tword* q = P.q + seq_off(P, n, l, P.QD) + r;
         st_tag(q, y0, tag);
         st_tag(q + 1, y1, tag);
       } else {
@@ -1231,7 +1274,7 @@ __device__ __forceinline__ void epi_pair_b(const Params& P, const Ctx& c, int l,
         const int hk = rr / P.D;
         uint16_t* dst = P.kcache + ((seq_off(P, n, l, P.NKV) + hk) * P.S + c.pos) * P.D + j;
         *reinterpret_cast<uint32_t*>(dst) = (uint32_t)k0 | ((uint32_t)k1 << 16);
-        uint64_t* kv = P.kvcur + seq_off(P, n, l, 2 * P.KVD) + rr;
+        tword* kv = P.kvcur + seq_off(P, n, l, 2 * P.KVD) + rr;
         st_tag(kv, bf16_to_f32(k0), tag);
         st_tag(kv + 1, bf16_to_f32(k1), tag);
       }
@@ -1241,7 +1284,7 @@ __device__ __forceinline__ void epi_pair_b(const Params& P, const Ctx& c, int l,
       const uint16_t b0 = f32_to_bf16(v0), b1 = f32_to_bf16(v1);
       uint16_t* dst = P.vcache + ((seq_off(P, n, l, P.NKV) + hv) * P.S + c.pos) * P.D + j;
       *reinterpret_cast<uint32_t*>(dst) = (uint32_t)b0 | ((uint32_t)b1 << 16);
-      uint64_t* kv = P.kvcur + seq_off(P, n, l, 2 * P.KVD) + P.KVD + rr;
+      tword* kv = P.kvcur + seq_off(P, n, l, 2 * P.KVD) + P.KVD + rr;
       st_tag(kv, bf16_to_f32(b0), tag);
       st_tag(kv + 1, bf16_to_f32(b1), tag);
     }
@@ -1265,7 +1308,7 @@ __device__ __forceinline__ void epi_row_b(const Params& P, const Ctx& c, const T
   } else {
     const int nr = (int)(t.a1 - t.a0) * kTileRows;
     const int k = r - (int)t.a0 * kTileRows;
-    uint64_t* dst = (OP == OP_OPROJ ? P.x_attn : P.x_ffn) + seq_off(P, n, l, P.H) + r;
+    tword* dst = (OP == OP_OPROJ ? P.x_attn : P.x_ffn) + seq_off(P, n, l, P.H) + r;
     st_tag(dst, c.res[n * nr + k] + v, c.epoch);
   }
 }
@@ -1291,7 +1334,7 @@ __device__ __forceinline__ void lm_finish_b(const Params& P, Ctx& c, const Task&
     const int n = c.wave;
     uint64_t k = 0;
     for (int w = c.lane; w < P.num_wgs; w += 64) {
-      const uint64_t x = ld_tag(P.amax + (size_t)n * P.num_wgs + w);
+      const uint64_t x = ld_u64_agent(P.amax + (size_t)n * P.num_wgs + w);
       k = x > k ? x : k;
     }
 #pragma unroll
@@ -1331,7 +1374,7 @@ __device__ __forceinline__ bool gemm_task(const Params& P, Ctx& c, Stream& st, c
       }
       __syncthreads();
     } else {
-      const uint64_t* src = OP == OP_GU ? P.x_attn + (size_t)l * P.H
+      const tword* src = OP == OP_GU ? P.x_attn + (size_t)l * P.H
                                         : P.x_ffn + (size_t)(OP == OP_LM ? P.L - 1 : l - 1) * P.H;
       if (!stage_batch(P, c, c.act, stride, src, (size_t)P.L * P.H, 0, P.H, P.H, s)) return false;
     }
@@ -1349,21 +1392,21 @@ __device__ __forceinline__ bool gemm_task(const Params& P, Ctx& c, Stream& st, c
         const int tok = token_of(P, c, n, s, false);
         v = bf16_to_f32(P.embed[(size_t)tok * P.H + r0 + k]);
       } else {
-        const uint64_t* rsrc = (OP == OP_OPROJ ? P.x_ffn + seq_off(P, n, l - 1, P.H) : P.x_attn + seq_off(P, n, l, P.H)) + r0 + k;
-        uint64_t rw = ld_tag(rsrc);
+        const tword* rsrc = (OP == OP_OPROJ ? P.x_ffn + seq_off(P, n, l - 1, P.H) : P.x_attn + seq_off(P, n, l, P.H)) + r0 + k;
+        tword rw = ld_tag(rsrc);
         uint64_t t0 = 0;
-        while ((uint32_t)(rw >> 32) != c.epoch) {
-          if (poll_stop(P, t0, s, (uint32_t)(rw >> 32))) {
+        while (!tag_ready(rw, c.epoch)) {
+          if (poll_stop(P, t0, s, tag_of(rw))) {
             c.flags[0] = 1;
             break;
           }
           rw = ld_tag(rsrc);
         }
-        v = __uint_as_float((uint32_t)rw);
+        v = tag_value(rw);
       }
       c.res[i] = v;
     }
-    const uint64_t* src = OP == OP_OPROJ ? P.o + (size_t)l * P.QD : P.h + (size_t)l * P.F;
+    const tword* src = OP == OP_OPROJ ? P.o + (size_t)l * P.QD : P.h + (size_t)l * P.F;
     const int kfull = OP == OP_OPROJ ? P.QD : P.F;
     const int kc0 = kfull < ch * kTileCols ? kfull : ch * kTileCols;
     if (!stage_batch(P, c, c.act, stride, src, (size_t)P.L * kfull, 0, kc0, ch * kTileCols, s)) return false;
@@ -1381,7 +1424,7 @@ __device__ __forceinline__ bool gemm_task(const Params& P, Ctx& c, Stream& st, c
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int cc = 0; cc < nc; ++cc) {
     if (cc > 0) {  // next chunk of the activation (one item per wave: acc carries over)
-      const uint64_t* src = OP == OP_OPROJ ? P.o + (size_t)l * P.QD : P.h + (size_t)l * P.F;
+      const tword* src = OP == OP_OPROJ ? P.o + (size_t)l * P.QD : P.h + (size_t)l * P.F;
       const int kfull = OP == OP_OPROJ ? P.QD : P.F;
       const int kcc = min(ch * kTileCols, kfull - cc * ch * kTileCols);
       if (!stage_batch(P, c, c.act, stride, src, (size_t)P.L * kfull, cc * ch * kTileCols, kcc, ch * kTileCols, s))
@@ -1644,7 +1687,7 @@ __device__ __forceinline__ bool attn_task_b(const Params& P, Ctx& c, const Task&
       Ls = fmaf(e, wl[w * G + h], Ls);
     }
   }
-  uint64_t* o = P.o + seq_off(P, n, l, P.QD) + (size_t)g * G * D;
+  tword* o = P.o + seq_off(P, n, l, P.QD) + (size_t)g * G * D;
   if (C == 1) {
     if (c.tid < G * D) st_tag(o + c.tid, A / Ls, c.epoch);
     return true;

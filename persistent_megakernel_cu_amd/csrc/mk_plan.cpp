@@ -55,7 +55,8 @@ int plan_build(const mk_config& c, int W, Plan& p) {
     return fail(p, MK_E_INVAL, "dimensions must be positive (n_layers >= 0)");
   if (c.n_heads % c.n_kv_heads != 0) return fail(p, MK_E_INVAL, "n_heads must be a multiple of n_kv_heads");
   if (c.head_dim != 64 && c.head_dim != 128) return fail(p, MK_E_UNSUPPORTED, "head_dim must be 64 or 128");
-  if (c.hidden % 2 != 0 || c.vocab % 2 != 0) return fail(p, MK_E_UNSUPPORTED, "hidden and vocab must be even");
+  if (c.hidden % 4 != 0 || c.ffn % 4 != 0 || c.vocab % 2 != 0)
+    return fail(p, MK_E_UNSUPPORTED, "hidden and ffn must be multiples of 4, vocab even");
   {
     const int grp = c.n_heads / c.n_kv_heads;
     if (grp != 1 && grp != 2 && grp != 4) return fail(p, MK_E_UNSUPPORTED, "1, 2 or 4 query heads per kv head");
