@@ -1207,13 +1207,36 @@ __device__ __forceinline__ int token_of(const Params& P, const Ctx& c, int n, in
 // [H, Hp)), so that W . rmsnorm(x_n) = rs[n] * (W . dst_n).
 __device__ __forceinline__ void norm_batch(const Params& P, Ctx& c, float* dst, int stride, const float* g,
                                            float* rsb) {
+  // lane: 4 consecutive columns per step of 256 (H and Hp are multiples of 4);
+  // the gains of 4 steps are loaded before their LDS updates, so global loads
+  // are not serialised behind LDS stores
   if (c.wave < P.B) {
     float* x = dst + c.wave * stride;
     float ss = 0.f;
-    for (int k = c.lane; k < P.H; k += 64) ss = fmaf(x[k], x[k], ss);
+    for (int k = c.lane * 4; k < P.H; k += 256) {
+      const float4 v = *reinterpret_cast<const float4*>(x + k);
+      ss = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss))));
+    }
     ss = wave_sum(ss);
     if (c.lane == 0) rsb[c.wave] = rsqrtf(ss / (float)P.H + P.eps);
-    for (int k = c.lane; k < P.Hp; k += 64) x[k] = k < P.H ? x[k] * g[k] : 0.f;
+    for (int k0 = c.lane * 4; k0 < P.Hp; k0 += 4 * 256) {
+      float4 gv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int k = k0 + u * 256;
+        gv[u] = k < P.H ? *reinterpret_cast<const float4*>(g + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int k = k0 + u * 256;
+        if (k < P.Hp) {  // padding columns [H, Hp) become zero whatever they held
+          float4 v = *reinterpret_cast<const float4*>(x + k);
+          v = k < P.H ? make_float4(v.x * gv[u].x, v.y * gv[u].y, v.z * gv[u].z, v.w * gv[u].w)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+          *reinterpret_cast<float4*>(x + k) = v;
+        }
+      }
+    }
   }
   __syncthreads();
 }
