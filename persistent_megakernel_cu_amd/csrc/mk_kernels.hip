@@ -851,13 +851,17 @@ __device__ __forceinline__ float slice_sum(float a) {
   return a;
 }
 
-// Sum over the position groups of a wave (lanes with equal lane % NT).
+// Sum over the position groups of a wave (lanes with equal lane % NT):
+// lane ^ 8 by DPP row rotation, lane ^ 16 and lane ^ 32 by the row and half
+// swaps of gfx950 (v_permlane16_swap / v_permlane32_swap), all VALU.  Every
+// lane ends with the same sum, formed in the same order.
 template <int NT>
 __device__ __forceinline__ float group_sum(float a) {
   if (NT == 8) a += dpp<0x128>(a);  // row_ror:8 == lane ^ 8 inside a row of 16
-  a += __shfl_xor(a, 16);
-  a += __shfl_xor(a, 32);
-  return a;
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+  a = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+  return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
