@@ -52,7 +52,7 @@ Workspace layout_workspace(const Plan& p) {
   w.o = take(cur, B * L * p.QD * 4);
   w.h = take(cur, B * L * p.F * 4);
   w.attn_part = take(cur, B * L * p.NKV * p.C * p.G * (p.D + 2) * 4);
-  w.attn_ctr = take(cur, B * L * p.NKV * 4);
+  w.attn_ctr = take(cur, B * L * p.NKV * p.G * 4);
   w.amax = take(cur, B * p.W * 8);
   w.amax_ctr = take(cur, B * 4);
   w.tokerr = take(cur, B * 4);
@@ -124,6 +124,7 @@ Params make_params(mk_handle* h) {
   P.eps = h->cfg.rms_eps;
   P.qscale = (float)(1.0 / std::sqrt((double)p.D));
   P.attn_chunks = p.C;
+  P.attn_gt = p.G / p.attn_slices;
   P.arena = h->arena;
   P.lm = h->lm;
   P.embed = h->embed;

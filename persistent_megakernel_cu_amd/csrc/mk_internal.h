@@ -64,7 +64,8 @@ constexpr int kStagesPerLayer = 5;
 //            is the whole pair and one wave finishes it; otherwise an item is
 //            a run of nu >> kslog units inside one row, and the partial sums
 //            of a pair's items are added in LDS in item order.
-//  OP_ATTN : a0 = kv head, a1 = chunk index, nu = sequence of the batch.
+//  OP_ATTN : a0 = kv head, a1 = chunk index, nu = sequence of the batch,
+//            kslog = slice of the kv head's query heads (batch 1).
 //  Batched plans: GEMM tasks cover row blocks [a0, a1) of 16 rows; nu is the
 //            number of 32-column tiles of a row; each block's tiles are cut
 //            into 2^kslog parts (split over waves, summed in LDS).
@@ -106,6 +107,7 @@ struct Params {
   float eps;
   float qscale;          // 1 / sqrt(head_dim)
   int32_t attn_chunks;
+  int32_t attn_gt;       // query heads per attention task (G, or 1 when each head has its own task)
 
   // weights
   const char* arena;     // packed bf16 matrices (byte base)
@@ -125,7 +127,7 @@ struct Params {
   uint32_t* o;           // [B][L][QD]  attention output
   uint32_t* h;           // [B][L][F]   SwiGLU hidden
   float* attn_part;      // [B][L][NKV][C][G*(D+2)] split-KV partials
-  uint32_t* attn_ctr;    // [B][L][NKV] merge counters (epoch * C per step)
+  uint32_t* attn_ctr;    // [B][L][NKV][G] merge counters per head slice (epoch * C per step)
   uint64_t* amax;        // [B][num_wgs] argmax keys
   uint32_t* amax_ctr;    // [B] argmax counters (epoch * tasks per step)
   uint32_t* tokerr;      // [B] epoch of the last bad input token

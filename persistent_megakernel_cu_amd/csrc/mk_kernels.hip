@@ -868,13 +868,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
 }
 
-template <int G, int D>
+template <int GT, int D>
 __device__ __forceinline__ bool attn_task(const Params& P, Ctx& c, const Task& t, int s) {
   constexpr int NT = D / 8;                 // threads per K/V row
   constexpr int PPP = kThreads / NT;        // positions per pass
   constexpr int NPASS = kMaxChunk / PPP;    // passes over a full chunk
   const int l = t.layer, g = (int)t.a0, ch = (int)t.a1;
   const int C = P.attn_chunks;
+  const int GQ = P.G;                      // query heads of the kv head
+  const int slice = (int)t.kslog;          // this task's heads: [slice * GT, + GT)
+  const int hq0 = slice * GT;
   const int n = c.pos + 1;
   const int len0 = (n + C - 1) / C;
   const int t0 = min(n, ch * len0), t1 = min(n, t0 + len0);
@@ -894,14 +897,14 @@ __device__ __forceinline__ bool attn_task(const Params& P, Ctx& c, const Task& t
     vr[j] = *reinterpret_cast<const uint4*>(P.vcache + o);
   }
 
-  float* qs = c.act;                       // [G][D], pre-scaled by 1/sqrt(D)
-  float* kcur = qs + G * D;                // [D]
+  float* qs = c.act;                       // [GT][D], pre-scaled by 1/sqrt(D)
+  float* kcur = qs + GT * D;               // [D]
   float* vcur = kcur + D;                  // [D]
-  float* wpart = vcur + D;                 // [kWaves][G][D]
-  float* wm = wpart + kWaves * G * D;      // [kWaves][G] per-wave max
-  float* wl = wm + kWaves * G;             // [kWaves][G] per-wave sum
+  float* wpart = vcur + D;                 // [kWaves][GT][D]
+  float* wm = wpart + kWaves * GT * D;     // [kWaves][GT] per-wave max
+  float* wl = wm + kWaves * GT;            // [kWaves][GT] per-wave sum
   {
-    const Seg seg[3] = {{qs, P.q + (size_t)l * P.QD + (size_t)g * G * D, G * D, P.qscale},
+    const Seg seg[3] = {{qs, P.q + (size_t)l * P.QD + (size_t)(g * GQ + hq0) * D, GT * D, P.qscale},
                         {kcur, P.kvcur + (size_t)l * 2 * P.KVD + (size_t)g * D, D, 1.f},
                         {vcur, P.kvcur + ((size_t)l * 2 + 1) * P.KVD + (size_t)g * D, D, 1.f}};
     if (!stage_tagged(P, c, seg, s)) return false;
@@ -930,10 +933,10 @@ __device__ __forceinline__ bool attn_task(const Params& P, Ctx& c, const Task& t
     }
   }
 
-  float acc[G][8];
-  float wmax[G], wsum[G];
+  float acc[GT][8];
+  float wmax[GT], wsum[GT];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
+  for (int h = 0; h < GT; ++h) {
     const float4 qa = *reinterpret_cast<const float4*>(qs + h * D + ds * 8);
     const float4 qb = *reinterpret_cast<const float4*>(qs + h * D + ds * 8 + 4);
     float sc[NPASS];
@@ -967,22 +970,22 @@ __device__ __forceinline__ bool attn_task(const Params& P, Ctx& c, const Task& t
     wmax[h] = m;
   }
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+  for (int h = 0; h < GT; ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = group_sum<NT>(acc[h][e]);
   if (c.lane < NT) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float* dst = wpart + (c.wave * G + h) * D + ds * 8;
+    for (int h = 0; h < GT; ++h) {
+      float* dst = wpart + (c.wave * GT + h) * D + ds * 8;
       *reinterpret_cast<float4*>(dst) = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
       *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
     }
   }
   if (c.lane == 0) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      wm[c.wave * G + h] = wmax[h];
-      wl[c.wave * G + h] = wsum[h];
+    for (int h = 0; h < GT; ++h) {
+      wm[c.wave * GT + h] = wmax[h];
+      wl[c.wave * GT + h] = wsum[h];
     }
   }
   mark_wave(c);
@@ -992,49 +995,51 @@ __device__ __forceinline__ bool attn_task(const Params& P, Ctx& c, const Task& t
   // merge the waves in order: max, then rescaled sums
   const int h = c.tid / D, d = c.tid % D;
   float A = 0.f, Ls = 0.f, M = -__builtin_inff();
-  if (c.tid < G * D) {
+  if (c.tid < GT * D) {
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wm[w * G + h]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wm[w * GT + h]);
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float mw = wm[w * G + h];
+      const float mw = wm[w * GT + h];
       const float e = mw == -__builtin_inff() ? 0.f : __expf(mw - M);
-      A = fmaf(e, wpart[(w * G + h) * D + d], A);
-      Ls = fmaf(e, wl[w * G + h], Ls);
+      A = fmaf(e, wpart[(w * GT + h) * D + d], A);
+      Ls = fmaf(e, wl[w * GT + h], Ls);
     }
   }
-  tword* o = P.o + (size_t)l * P.QD + (size_t)g * G * D;
+  tword* o = P.o + (size_t)l * P.QD + (size_t)(g * GQ + hq0) * D;
   if (C == 1) {
-    if (c.tid < G * D) st_tag(o + c.tid, A / Ls, c.epoch);
+    if (c.tid < GT * D) st_tag(o + c.tid, A / Ls, c.epoch);
     return true;
   }
-  // publish this chunk's partial {m[G], l[G], acc[G][D]}; the last chunk of the head merges
-  const int stride = G * (D + 2);
+  // publish this chunk's partial of the task's heads into the kv head's
+  // record {m[GQ], l[GQ], acc[GQ][D]}; the last chunk of (kv head, slice) merges
+  const int stride = GQ * (D + 2);
+  const int hg = hq0 + h;                  // head inside the kv head's group
   float* mine = P.attn_part + (((size_t)l * P.NKV + g) * C + ch) * stride;
-  if (c.tid < G * D) st_f32_agent(mine + 2 * G + c.tid, A);
-  if (c.tid < G * D && d == 0) {
-    st_f32_agent(mine + h, M);
-    st_f32_agent(mine + G + h, Ls);
+  if (c.tid < GT * D) st_f32_agent(mine + 2 * GQ + hq0 * D + c.tid, A);
+  if (c.tid < GT * D && d == 0) {
+    st_f32_agent(mine + hg, M);
+    st_f32_agent(mine + GQ + hg, Ls);
   }
   wait_all_vmem();
   __syncthreads();
   if (c.tid == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(P.attn_ctr + (size_t)l * P.NKV + g, 1u, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t old = __hip_atomic_fetch_add(P.attn_ctr + ((size_t)l * P.NKV + g) * GQ + slice, 1u,
+                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     c.flags[1] = old == c.epoch * (uint32_t)C - 1u;
   }
   __syncthreads();
-  if (c.flags[1] && c.tid < G * D) {
+  if (c.flags[1] && c.tid < GT * D) {
     const float* base = P.attn_part + ((size_t)l * P.NKV + g) * C * stride;
     float MM = -__builtin_inff();
-    for (int k = 0; k < C; ++k) MM = fmaxf(MM, ld_f32_agent(base + (size_t)k * stride + h));
+    for (int k = 0; k < C; ++k) MM = fmaxf(MM, ld_f32_agent(base + (size_t)k * stride + hg));
     float LL = 0.f, AA = 0.f;
     for (int k = 0; k < C; ++k) {
       const float* pk = base + (size_t)k * stride;
-      const float mk = ld_f32_agent(pk + h);
+      const float mk = ld_f32_agent(pk + hg);
       const float e = mk == -__builtin_inff() ? 0.f : __expf(mk - MM);
-      LL = fmaf(e, ld_f32_agent(pk + G + h), LL);
-      AA = fmaf(e, ld_f32_agent(pk + 2 * G + c.tid), AA);
+      LL = fmaf(e, ld_f32_agent(pk + GQ + hg), LL);
+      AA = fmaf(e, ld_f32_agent(pk + 2 * GQ + hq0 * D + c.tid), AA);
     }
     st_tag(o + c.tid, AA / LL, c.epoch);
   }
@@ -1830,7 +1835,12 @@ __device__ __forceinline__ void run_stages(const Params& P, int s_begin, int s_e
         case OP_GU: ok = gemv_task<OP_GU>(P, c, st, t, s); break;
         case OP_DOWN: ok = gemv_task<OP_DOWN>(P, c, st, t, s); break;
         case OP_LM: ok = gemv_task<OP_LM>(P, c, st, t, s); break;
-        case OP_ATTN: ok = attn_task<G, D>(P, c, t, s); break;
+        case OP_ATTN:
+          if constexpr (G == 1)
+            ok = attn_task<1, D>(P, c, t, s);
+          else
+            ok = P.attn_gt == 1 ? attn_task<1, D>(P, c, t, s) : attn_task<G, D>(P, c, t, s);
+          break;
         default: break;
       }
     }

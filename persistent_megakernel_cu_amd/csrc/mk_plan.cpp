@@ -101,6 +101,9 @@ int plan_build(const mk_config& c, int W, Plan& p) {
   if ((int64_t)C * seqs_kv > W) C = std::max(1, W / seqs_kv);
   if ((int64_t)C * seqs_kv > W) return fail(p, MK_E_UNSUPPORTED, "more (sequence, kv head) pairs than workgroups");
   p.C = C;
+  // Batch 1: when there are workgroups to spare, every query head of a kv
+  // head gets its own attention task (no merge: heads are independent).
+  p.attn_slices = (!p.batched && (int64_t)seqs_kv * p.G * C <= W) ? p.G : 1;
   const int lmax = (p.S + C - 1) / C;  // longest chunk
   if (!p.batched && lmax > kMaxChunk) return fail(p, MK_E_UNSUPPORTED, "attention chunk longer than 256 positions");
 
@@ -190,28 +193,30 @@ int plan_build(const mk_config& c, int W, Plan& p) {
       gemm_stage(s0 + 0, OP_QKV, l, qkv_rows(p), (uint32_t)(p.Hp / kTileCols), p.off_qkv[l], 0);
     else
       gemv_stage(s0 + 0, OP_QKV, l, qkv_rows(p) / 2, (uint32_t)(2 * p.Hp / kUnitElems), p.off_qkv[l], 0);
-    // attention: task i = (sequence, kv head, chunk) on workgroup i
-    for (int i = 0; i < seqs_kv * C; ++i) {
+    // attention: task i = (sequence, kv head, query-head slice, chunk) on workgroup i
+    const int sl = p.attn_slices;
+    for (int i = 0; i < seqs_kv * sl * C; ++i) {
       Task& t = p.tape[(size_t)(s0 + 1) * W + i];
       t.op = OP_ATTN;
       t.layer = (uint16_t)l;
-      t.nu = (uint32_t)(i / (p.NKV * C));
-      t.a0 = (uint32_t)((i / C) % p.NKV);
+      t.nu = (uint32_t)(i / (p.NKV * sl * C));
+      t.a0 = (uint32_t)((i / (sl * C)) % p.NKV);
+      t.kslog = (uint32_t)((i / C) % sl);
       t.a1 = (uint32_t)(i % C);
-      t.ntasks = (uint32_t)(seqs_kv * C);
+      t.ntasks = (uint32_t)(seqs_kv * sl * C);
     }
     if (p.batched) {
-      const int gu_b0 = (seqs_kv * C * 8 <= W) ? seqs_kv * C : 0;
+      const int gu_b0 = (seqs_kv * C * 8 <= W) ? seqs_kv * C : 0;  // batched plans have one slice
       gemm_stage(s0 + 2, OP_OPROJ, l, p.H, (uint32_t)(p.QDp / kTileCols), p.off_o[l], 0);
       gemm_stage(s0 + 3, OP_GU, l, 2ull * p.F, (uint32_t)(p.Hp / kTileCols), p.off_gu[l], 0, gu_b0);
       gemm_stage(s0 + 4, OP_DOWN, l, p.H, (uint32_t)(p.Fp / kTileCols), p.off_down[l], 0);
       continue;
     }
     gemv_stage(s0 + 2, OP_OPROJ, l, p.H / 2, (uint32_t)(2 * p.QDp / kUnitElems), p.off_o[l], 0);
-    // When attention occupies few workgroups they sit out the gate/up stage:
-    // they reach it last (after attention and O-proj), and the down
-    // projection waits for the slowest gate/up task.
-    const int gu_b0 = (p.NKV * C * 8 <= W) ? p.NKV * C : 0;
+    // When attention occupies very few workgroups (at most 1/16 of them) they
+    // sit out the gate/up stage: they reach it last (after attention and
+    // O-proj), and the down projection waits for the slowest gate/up task.
+    const int gu_b0 = (p.NKV * sl * C * 16 <= W) ? p.NKV * sl * C : 0;
     gemv_stage(s0 + 3, OP_GU, l, p.F, (uint32_t)(2 * p.Hp / kUnitElems), p.off_gu[l], 0, gu_b0);
     gemv_stage(s0 + 4, OP_DOWN, l, p.H / 2, (uint32_t)(2 * p.Fp / kUnitElems), p.off_down[l], 0);
   }
@@ -281,13 +286,15 @@ int plan_validate(const Plan& p, std::string* why) {
     uint32_t count = 0;
     for (int b = 0; b < W; ++b) count += p.tape[(size_t)s * W + b].op != OP_NONE;
     if (kind == OP_ATTN) {
-      std::vector<int> seen((size_t)p.B * p.NKV * p.C, 0);
+      const int sl = p.attn_slices;
+      std::vector<int> seen((size_t)p.B * p.NKV * sl * p.C, 0);
       for (int b = 0; b < W; ++b) {
         const Task& t = p.tape[(size_t)s * W + b];
         if (t.op == OP_NONE) continue;
         if (t.op != OP_ATTN || t.layer != layer) return bad("attention stage holds another op");
-        if ((int)t.a0 >= p.NKV || (int)t.a1 >= p.C || (int)t.nu >= p.B) return bad("attention task out of range");
-        if (seen[((size_t)t.nu * p.NKV + t.a0) * p.C + t.a1]++) return bad("attention task repeated");
+        if ((int)t.a0 >= p.NKV || (int)t.a1 >= p.C || (int)t.nu >= p.B || (int)t.kslog >= sl)
+          return bad("attention task out of range");
+        if (seen[(((size_t)t.nu * p.NKV + t.a0) * sl + t.kslog) * p.C + t.a1]++) return bad("attention task repeated");
         if (t.ntasks != count) return bad("attention task count");
       }
       for (int v : seen)

@@ -18,6 +18,7 @@ struct Plan {
   int QD = 0, QDp = 0, KVD = 0, F = 0, Fp = 0, V = 0, S = 0, B = 0;
   int W = 0;       // persistent workgroups
   int C = 0;       // attention chunks per kv head (and sequence)
+  int attn_slices = 1;  // batch 1: attention tasks per (kv head, chunk), one per query head or 1
   bool batched = false;  // B > 1: tiled weights, MFMA tasks
   int stages = 0;  // kStagesPerLayer * L + 1
   bool tied = true;
