@@ -35,9 +35,9 @@ HBM_PEAK_GBPS = 8000.0
 # commands are in profiles/mk_persistent_llama1b_hbm_bytes.md).  They describe
 # the kernel sources whose hash is recorded; any other source gives null.
 MEASURED_TRAFFIC = {
-    "sources_sha256_prefix": "379c62f498e3f366",
-    "fetch_bytes": 2.5096e9,
-    "write_bytes": 7.05e6,
+    "sources_sha256_prefix": "916bce2858c7dd92",
+    "fetch_bytes": 2.5085e9,
+    "write_bytes": 6.14e6,
     "fetch_factor": 2.000,
     "write_factor": 1.000,
 }
