@@ -868,6 +868,49 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
 }
 
+// Merge of C chunk partials of one kv head, records of `stride` floats laid
+// out {m[GQ], l[GQ], acc[GQ][D]}, for the GT heads [h0, h0 + GT): the global
+// maximum first, then the rescaled sums, in chunk order.  Thread tid < GT * D
+// owns output element tid.  The {m, l} table goes through LDS (2 * C * GT
+// floats at tab, one load round trip for the whole workgroup); the
+// accumulators are loaded KG chunks at a time into registers, all KG loads in
+// flight together, so a merge costs 1 + C / KG memory round trips instead of
+// one per chunk.  Called by the whole workgroup (one barrier).
+template <int GT, int D, int KG>
+__device__ __forceinline__ void merge_chunks(const Ctx& c, const float* base, int C, int stride, int GQ,
+                                             int h0, float* tab, tword* o) {
+  const bool mine = c.tid < GT * D;
+  const int h = c.tid / D;
+  float av[KG];
+  for (int i = c.tid; i < C * GT; i += kThreads) {
+    const int k = i / GT, hh = i - k * GT;
+    const float* pk = base + (size_t)k * stride + h0 + hh;
+    tab[2 * i] = ld_f32_agent(pk);
+    tab[2 * i + 1] = ld_f32_agent(pk + GQ);
+  }
+  __syncthreads();
+  if (!mine) return;
+  float MM = -__builtin_inff();
+  for (int k = 0; k < C; ++k) MM = fmaxf(MM, tab[2 * (k * GT + h)]);
+  float LL = 0.f, AA = 0.f;
+  for (int k0 = 0; k0 < C; k0 += KG) {
+#pragma unroll
+    for (int u = 0; u < KG; ++u)
+      av[u] = k0 + u < C ? ld_f32_agent(base + (size_t)(k0 + u) * stride + 2 * GQ + h0 * D + c.tid) : 0.f;
+#pragma unroll
+    for (int u = 0; u < KG; ++u) {
+      const int k = k0 + u;
+      if (k < C) {
+        const float mk = tab[2 * (k * GT + h)];
+        const float e = mk == -__builtin_inff() ? 0.f : __expf(mk - MM);
+        LL = fmaf(e, tab[2 * (k * GT + h) + 1], LL);
+        AA = fmaf(e, av[u], AA);
+      }
+    }
+  }
+  st_tag(o + c.tid, AA / LL, c.epoch);
+}
+
 template <int GT, int D>
 __device__ __forceinline__ bool attn_task(const Params& P, Ctx& c, const Task& t, int s) {
   constexpr int NT = D / 8;                 // threads per K/V row
@@ -1029,20 +1072,10 @@ __device__ __forceinline__ bool attn_task(const Params& P, Ctx& c, const Task& t
     c.flags[1] = old == c.epoch * (uint32_t)C - 1u;
   }
   __syncthreads();
-  if (c.flags[1] && c.tid < GT * D) {
-    const float* base = P.attn_part + ((size_t)l * P.NKV + g) * C * stride;
-    float MM = -__builtin_inff();
-    for (int k = 0; k < C; ++k) MM = fmaxf(MM, ld_f32_agent(base + (size_t)k * stride + hg));
-    float LL = 0.f, AA = 0.f;
-    for (int k = 0; k < C; ++k) {
-      const float* pk = base + (size_t)k * stride;
-      const float mk = ld_f32_agent(pk + hg);
-      const float e = mk == -__builtin_inff() ? 0.f : __expf(mk - MM);
-      LL = fmaf(e, ld_f32_agent(pk + GQ + hg), LL);
-      AA = fmaf(e, ld_f32_agent(pk + 2 * GQ + hq0 * D + c.tid), AA);
-    }
-    st_tag(o + c.tid, AA / LL, c.epoch);
-  }
+  // the {m, l} table reuses wpart (free after the barrier above):
+  // 2 * C * GT <= kWaves * GT * D because C <= 256 <= 4 * D
+  if (c.flags[1])
+    merge_chunks<GT, D, 16>(c, P.attn_part + ((size_t)l * P.NKV + g) * C * stride, C, stride, GQ, hq0, wpart, o);
   return true;
 }
 
@@ -1739,20 +1772,7 @@ __device__ __forceinline__ bool attn_task_b(const Params& P, Ctx& c, const Task&
     c.flags[1] = old == c.epoch * (uint32_t)C - 1u;
   }
   __syncthreads();
-  if (c.flags[1] && c.tid < G * D) {
-    const float* basep = P.attn_part + head * C * stride;
-    float MM = -__builtin_inff();
-    for (int k = 0; k < C; ++k) MM = fmaxf(MM, ld_f32_agent(basep + (size_t)k * stride + h));
-    float LL = 0.f, AA = 0.f;
-    for (int k = 0; k < C; ++k) {
-      const float* pk = basep + (size_t)k * stride;
-      const float mk = ld_f32_agent(pk + h);
-      const float e = mk == -__builtin_inff() ? 0.f : __expf(mk - MM);
-      LL = fmaf(e, ld_f32_agent(pk + G + h), LL);
-      AA = fmaf(e, ld_f32_agent(pk + 2 * G + c.tid), AA);
-    }
-    st_tag(o + c.tid, AA / LL, c.epoch);
-  }
+  if (c.flags[1]) merge_chunks<G, D, 8>(c, P.attn_part + head * C * stride, C, stride, G, 0, wpart, o);
   return true;
 }
 

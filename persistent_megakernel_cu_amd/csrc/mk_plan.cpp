@@ -100,6 +100,9 @@ int plan_build(const mk_config& c, int W, Plan& p) {
   C = std::max(1, std::min(C, p.S));
   if ((int64_t)C * seqs_kv > W) C = std::max(1, W / seqs_kv);
   if ((int64_t)C * seqs_kv > W) return fail(p, MK_E_UNSUPPORTED, "more (sequence, kv head) pairs than workgroups");
+  // the merge keeps a {max, sum} pair per chunk and head in the LDS that
+  // held the eight waves' partial outputs
+  C = std::min(C, kWaves * p.D / 2);
   p.C = C;
   // Batch 1: when there are workgroups to spare, every query head of a kv
   // head gets its own attention task (no merge: heads are independent).
@@ -287,6 +290,7 @@ int plan_validate(const Plan& p, std::string* why) {
     for (int b = 0; b < W; ++b) count += p.tape[(size_t)s * W + b].op != OP_NONE;
     if (kind == OP_ATTN) {
       const int sl = p.attn_slices;
+      if (2 * p.C > kWaves * p.D) return bad("more attention chunks than the merge table holds");
       std::vector<int> seen((size_t)p.B * p.NKV * sl * p.C, 0);
       for (int b = 0; b < W; ++b) {
         const Task& t = p.tape[(size_t)s * W + b];
