@@ -19,9 +19,10 @@
 // release/acquire fence pair (L2 writeback + invalidate) costs ~20 us for a
 // 256-workgroup exchange, and 256 workgroups on one counter serialise to
 // ~4 us, while an agent-coherent 8-byte store/load round trip is ~0.6 us.
-// So every activation element travels as one 8-byte word {fp32 value, epoch}
-// written and read with agent-scope (sc1) accesses: the consumer polls the
-// data itself, no fence and no counter sits on the critical path.
+// So every activation element travels as one 4-byte tagged word (the fp32
+// value rounded to 24 bits, the step's epoch in the low byte) written and read
+// with agent-scope accesses: the consumer polls the data itself, no fence and
+// no counter sits on the critical path.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -255,15 +256,24 @@ __device__ __forceinline__ void latch_error(const Params& P, int code, int stage
   if (code == MK_E_TIMEOUT) __hip_atomic_store(P.abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Wall-clock ticks (100 MHz, 20 us) a wait runs before it checks the abort flag.
+constexpr uint64_t kAbortCheckTicks = 2000;
+
 // One poll iteration's bookkeeping; true when the wait must stop.
 __device__ __forceinline__ bool poll_stop(const Params& P, uint64_t& t0, int stage, uint32_t seen) {
   const uint64_t now = wall_clock64();
   if (t0 == 0) {
     t0 = now | 1;
-  } else if (now - t0 > P.watchdog_ticks) {
+    return false;
+  }
+  if (now - t0 > P.watchdog_ticks) {
     latch_error(P, MK_E_TIMEOUT, stage, seen);
     return true;
   }
+  // The abort flag is raised only by another workgroup's watchdog, long after
+  // any normal wait has ended: skip its coherent load (one per wave and poll
+  // round) during the first kAbortCheckTicks of a wait.
+  if (now - t0 < kAbortCheckTicks) return false;
   return ld_u32_agent(P.abort_flag) != 0;
 }
 
