@@ -31,7 +31,7 @@ namespace {
 constexpr uint32_t kEpochLimit = 1u << 20;
 
 struct Workspace {
-  size_t x_attn, x_ffn, q, kvcur, o, h, attn_part, attn_ctr, amax, amax_ctr, tokerr, abort_flag, status, dargs;
+  size_t x_attn, x_ffn, q, kvcur, o, h, kpart, attn_part, attn_ctr, amax, amax_ctr, tokerr, abort_flag, status, dargs;
   size_t bytes;
 };
 
@@ -51,6 +51,7 @@ Workspace layout_workspace(const Plan& p) {
   w.kvcur = take(cur, B * L * 2 * p.KVD * 4);
   w.o = take(cur, B * L * p.QD * 4);
   w.h = take(cur, B * L * p.F * 4);
+  w.kpart = take(cur, B * L * p.H * 4);
   w.attn_part = take(cur, B * L * p.NKV * p.C * p.G * (p.D + 2) * 4);
   w.attn_ctr = take(cur, B * L * p.NKV * p.G * 4);
   w.amax = take(cur, B * p.W * 8);
@@ -140,6 +141,7 @@ Params make_params(mk_handle* h) {
   P.kvcur = reinterpret_cast<uint32_t*>(ws + w.kvcur);
   P.o = reinterpret_cast<uint32_t*>(ws + w.o);
   P.h = reinterpret_cast<uint32_t*>(ws + w.h);
+  P.kpart = reinterpret_cast<uint32_t*>(ws + w.kpart);
   P.attn_part = reinterpret_cast<float*>(ws + w.attn_part);
   P.attn_ctr = reinterpret_cast<uint32_t*>(ws + w.attn_ctr);
   P.amax = reinterpret_cast<uint64_t*>(ws + w.amax);

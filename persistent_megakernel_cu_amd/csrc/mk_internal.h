@@ -68,7 +68,16 @@ constexpr int kStagesPerLayer = 5;
 //            kslog = slice of the kv head's query heads (batch 1).
 //  Batched plans: GEMM tasks cover row blocks [a0, a1) of 16 rows; nu is the
 //            number of 32-column tiles of a row; each block's tiles are cut
-//            into 2^kslog parts (split over waves, summed in LDS).
+//            into 2^kslog parts (split over waves, summed in LDS).  A down
+//            projection with fewer blocks than half the workgroups gives each
+//            block to two workgroups (region bit kRegionSplit), each walking
+//            half of the row's chunks; the second half (kRegionHalf1) hands its
+//            partial sums to the first, which adds them in that order.
+// Bits of Task::region.
+constexpr uint8_t kRegionLm = 1;      // weights are the LM head, not the arena
+constexpr uint8_t kRegionSplit = 2;   // batched: the block's chunks are split over two workgroups
+constexpr uint8_t kRegionHalf1 = 4;   // batched: this task walks the second half of the chunks
+
 struct Task {
   uint8_t op;
   uint8_t region;
@@ -126,6 +135,7 @@ struct Params {
   uint32_t* kvcur;       // [B][L][2][KVD] this step's bf16-rounded k, v
   uint32_t* o;           // [B][L][QD]  attention output
   uint32_t* h;           // [B][L][F]   SwiGLU hidden
+  uint32_t* kpart;       // [B][L][H]   second-half partial sums of split down tasks
   float* attn_part;      // [B][L][NKV][C][G*(D+2)] split-KV partials
   uint32_t* attn_ctr;    // [B][L][NKV][G] merge counters per head slice (epoch * C per step)
   uint64_t* amax;        // [B][num_wgs] argmax keys

@@ -530,7 +530,7 @@ __device__ __forceinline__ void loader_seek(const Params& P, Stream& st, int s, 
         st.lu = 0;
         st.la0 = t.a0;
         st.lnu = t.nu;
-        st.lbase = (t.region ? P.lm : P.arena) + t.wofs;
+        st.lbase = ((t.region & kRegionLm) ? P.lm : P.arena) + t.wofs;
         return;
       }
     }
@@ -1121,10 +1121,12 @@ __device__ __forceinline__ void loader_seek_b(const Params& P, Stream& st, int s
         st.lu = 0;
         st.la0 = t.a0;
         st.lnu = t.nu;            // tiles per row
-        st.lc = 0;
-        st.lnc = t.nu / ch;
+        // chunks [lc, lnc): all of them, or this task's half of a split block
+        const uint32_t nc = t.nu / ch;
+        st.lc = (t.region & kRegionHalf1) ? nc / 2 : 0;
+        st.lnc = (t.region & kRegionSplit) ? st.lc + nc / 2 : nc;
         st.lch = ch;
-        st.lbase = (t.region ? P.lm : P.arena) + t.wofs;
+        st.lbase = ((t.region & kRegionLm) ? P.lm : P.arena) + t.wofs;
         return;
       }
     }
@@ -1147,7 +1149,7 @@ __device__ __forceinline__ void loader_issue_b(const Params& P, Stream& st, int 
     st.litem += kWaves;
     if (st.litem >= st.lnitems) {
       st.litem = (uint32_t)wave;
-      if (++st.lc == st.lnc) loader_seek_b(P, st, st.ls + 1, wave);
+      if (++st.lc >= st.lnc) loader_seek_b(P, st, st.ls + 1, wave);
     }
   }
 }
@@ -1431,6 +1433,9 @@ __device__ __forceinline__ bool gemm_task(const Params& P, Ctx& c, Stream& st, c
   const int stride = P.act_stride;
   float* rsb = c.red + 16;  // [kMaxBatch] RMSNorm scales of the sequences
   const int kt = (int)t.nu, ch = kt < kChunkTiles ? kt : kChunkTiles, nc = kt / ch;
+  // chunks [cb, ce) of every row: all, or one half of a block split over two workgroups
+  const bool split = (t.region & kRegionSplit) != 0, half1 = (t.region & kRegionHalf1) != 0;
+  const int cb = half1 ? nc / 2 : 0, ce = split ? cb + nc / 2 : nc;
   const int ks = 1 << t.kslog, upc = ch >> t.kslog;
   const int nitems = (int)(t.a1 - t.a0) << t.kslog;
   const int nblk = (int)(t.a1 - t.a0);
@@ -1483,8 +1488,9 @@ __device__ __forceinline__ bool gemm_task(const Params& P, Ctx& c, Stream& st, c
     }
     const tword* src = OP == OP_OPROJ ? P.o + (size_t)l * P.QD : P.h + (size_t)l * P.F;
     const int kfull = OP == OP_OPROJ ? P.QD : P.F;
-    const int kc0 = kfull < ch * kTileCols ? kfull : ch * kTileCols;
-    if (!stage_batch(P, c, c.act, stride, src, (size_t)P.L * kfull, 0, kc0, ch * kTileCols, s)) return false;
+    const int col0 = cb * ch * kTileCols;
+    const int kc0 = min(ch * kTileCols, kfull - col0);
+    if (!stage_batch(P, c, c.act, stride, src, (size_t)P.L * kfull, col0, kc0, ch * kTileCols, s)) return false;
     if (c.flags[0]) return false;
     if (c.tid < P.B) rsb[c.tid] = 1.f;
     __syncthreads();
@@ -1497,8 +1503,8 @@ __device__ __forceinline__ bool gemm_task(const Params& P, Ctx& c, Stream& st, c
   const int kq = (c.lane >> 4) * 8;
   LmBestB best{-__builtin_inff(), -1};
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int cc = 0; cc < nc; ++cc) {
-    if (cc > 0) {  // next chunk of the activation (one item per wave: acc carries over)
+  for (int cc = cb; cc < ce; ++cc) {
+    if (cc > cb) {  // next chunk of the activation (one item per wave: acc carries over)
       const tword* src = OP == OP_OPROJ ? P.o + (size_t)l * P.QD : P.h + (size_t)l * P.F;
       const int kfull = OP == OP_OPROJ ? P.QD : P.F;
       const int kcc = min(ch * kTileCols, kfull - cc * ch * kTileCols);
@@ -1525,7 +1531,7 @@ __device__ __forceinline__ bool gemm_task(const Params& P, Ctx& c, Stream& st, c
         b_operand(c.act, stride, n_col, live, col0 + u * kTileCols + kq, hi, lo);
         acc = mfma_tile(w, hi, lo, acc);
       }
-      if (cc != nc - 1) continue;
+      if (cc != ce - 1) continue;
       const int blk = (int)t.a0 + (i >> t.kslog);
       if (ks == 1) {
         // lane: rows 4 * (lane / 16) + 0..3 of the block, sequence lane % 16
@@ -1572,10 +1578,31 @@ __device__ __forceinline__ bool gemm_task(const Params& P, Ctx& c, Stream& st, c
           // reduced values back into the first part's tile for the argmax scan
           c.part[(size_t)(j * ks) * (kTileRows * 16) + q * 16 + n] = v * rsb[n];
           P.logits[(size_t)n * P.V + ((int)t.a0 + j) * kTileRows + q] = v * rsb[n];
+        } else if (OP == OP_DOWN && split) {
+          // the second half hands its sums over; the first half adds them to its own
+          tword* kp = P.kpart + seq_off(P, n, l, P.H) + ((int)t.a0 + j) * kTileRows + q;
+          if (half1) {
+            st_tag(kp, v, c.epoch);
+            continue;
+          }
+          tword w = ld_tag(kp);
+          uint64_t t0 = 0;
+          while (!tag_ready(w, c.epoch)) {
+            if (poll_stop(P, t0, s, tag_of(w))) {
+              c.flags[0] = 1;
+              break;
+            }
+            w = ld_tag(kp);
+          }
+          epi_row_b<OP>(P, c, t, l, ((int)t.a0 + j) * kTileRows + q, n, v + tag_value(w), rsb, best);
         } else {
           epi_row_b<OP>(P, c, t, l, ((int)t.a0 + j) * kTileRows + q, n, v, rsb, best);
         }
       }
+    }
+    if (OP == OP_DOWN && split) {  // a watchdog stop while waiting for the second half
+      __syncthreads();
+      if (c.flags[0]) return false;
     }
   }
   mark(c, 2);

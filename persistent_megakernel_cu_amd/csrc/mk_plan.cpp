@@ -170,6 +170,26 @@ int plan_build(const mk_config& c, int W, Plan& p) {
     const uint64_t blocks = rows / kTileRows;
     const int nw = W - b0;
     const uint32_t ch = std::min<uint32_t>(ktiles, kChunkTiles);
+    const uint32_t nc = ktiles / ch;
+    if (op == OP_DOWN && b0 == 0 && 2 * blocks <= (uint64_t)W && nc >= 2 && nc % 2 == 0) {
+      // two workgroups per block, one per half of the row's chunks
+      uint32_t k = 0;
+      while ((2u << k) <= (uint32_t)kWaves && (ch >> (k + 1)) > 0 && ch % (2u << k) == 0) ++k;
+      for (uint64_t i = 0; i < 2 * blocks; ++i) {
+        Task& t = p.tape[(size_t)s * W + i];
+        t.op = op;
+        t.region = (uint8_t)(region | kRegionSplit | ((i & 1) ? kRegionHalf1 : 0));
+        t.layer = (uint16_t)layer;
+        t.a0 = (uint32_t)(i / 2);
+        t.a1 = t.a0 + 1;
+        t.nu = ktiles;
+        t.wofs = wofs;
+        t.ntasks = (uint32_t)(2 * blocks);
+        t.kslog = k;
+        max_res_rows = std::max(max_res_rows, kTileRows);
+      }
+      return;
+    }
     uint32_t n = 0;
     for (int i = 0; i < nw; ++i) n += blocks * (uint64_t)(i + 1) / nw > blocks * (uint64_t)i / nw;
     for (int i = 0; i < nw; ++i) {
@@ -317,16 +337,33 @@ int plan_validate(const Plan& p, std::string* why) {
       }
       const uint64_t ch = std::min<uint64_t>(kt, kChunkTiles);
       uint64_t next = 0;
+      int half0 = -1;  // workgroup holding the first half of a split block, until its second half
       for (int b = 0; b < W; ++b) {
         const Task& t = p.tape[(size_t)s * W + b];
         if (t.op == OP_NONE) continue;
         if (t.op != kind || t.layer != layer) return bad("stage holds another op");
-        if (t.a0 != next || t.a1 <= t.a0) return bad("row blocks not tiled exactly");
-        next = t.a1;
+        if (t.region & kRegionSplit) {
+          // split block: the first half, then the second half on the next workgroup
+          if (kind != OP_DOWN || t.a1 != t.a0 + 1 || t.kslog == 0 || (kt / ch) % 2 != 0)
+            return bad("split task geometry");
+          if (!(t.region & kRegionHalf1)) {
+            if (half0 >= 0 || t.a0 != next) return bad("split blocks not tiled exactly");
+            half0 = b;
+          } else {
+            const Task& f = p.tape[(size_t)s * W + (half0 < 0 ? 0 : half0)];
+            if (half0 != b - 1 || f.a0 != t.a0) return bad("split block without its first half");
+            half0 = -1;
+            next = t.a1;
+          }
+        } else {
+          if (half0 >= 0) return bad("split block without its second half");
+          if (t.a0 != next || t.a1 <= t.a0) return bad("row blocks not tiled exactly");
+          next = t.a1;
+        }
         if (t.nu != kt || t.wofs != wofs) return bad("task geometry");
         if ((uint64_t)t.a1 * kt * kUnitBytes > region_bytes) return bad("task reads past its matrix");
         if (t.ntasks != count) return bad("task count");
-        if (t.region != (kind == OP_LM ? 1 : 0)) return bad("weight region");
+        if ((t.region & kRegionLm) != (kind == OP_LM ? kRegionLm : 0)) return bad("weight region");
         const uint64_t ks = 1ull << t.kslog, items = (uint64_t)(t.a1 - t.a0) * ks;
         if (kt % ch != 0 || ch % ks != 0) return bad("parts do not divide the chunks");
         if (ks > 1 && items > (uint64_t)kWaves) return bad("split blocks need one item per wave");
@@ -334,6 +371,7 @@ int plan_validate(const Plan& p, std::string* why) {
         if ((kind == OP_OPROJ || kind == OP_DOWN) && (uint64_t)p.B * (t.a1 - t.a0) * kTileRows > (uint64_t)p.res_floats)
           return bad("residual rows exceed LDS");
       }
+      if (half0 >= 0) return bad("split block without its second half");
       if (next != rows / kTileRows) return bad("row blocks not covered");
       continue;
     }
