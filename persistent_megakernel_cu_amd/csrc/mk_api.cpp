@@ -51,7 +51,7 @@ Workspace layout_workspace(const Plan& p) {
   w.kvcur = take(cur, B * L * 2 * p.KVD * 4);
   w.o = take(cur, B * L * p.QD * 4);
   w.h = take(cur, B * L * p.F * 4);
-  w.kpart = take(cur, B * L * p.H * 4);
+  w.kpart = take(cur, B * L * 2 * p.H * 4);
   w.attn_part = take(cur, B * L * p.NKV * p.C * p.G * (p.D + 2) * 4);
   w.attn_ctr = take(cur, B * L * p.NKV * p.G * 4);
   w.amax = take(cur, B * p.W * 8);

@@ -69,10 +69,18 @@ constexpr int kStagesPerLayer = 5;
 //  Batched plans: GEMM tasks cover row blocks [a0, a1) of 16 rows; nu is the
 //            number of 32-column tiles of a row; each block's tiles are cut
 //            into 2^kslog parts (split over waves, summed in LDS).  A down
-//            projection with fewer blocks than half the workgroups gives each
-//            block to two workgroups (region bit kRegionSplit), each walking
-//            half of the row's chunks; the second half (kRegionHalf1) hands its
-//            partial sums to the first, which adds them in that order.
+//            or down projection with at most half as many blocks as
+//            workgroups gives each block to two workgroups (region bit
+//            kRegionSplit), each walking half of the row's chunks (a row of
+//            one chunk is walked as two half-width chunks); the second half
+//            (kRegionHalf1) hands its partial sums to the first, which adds
+//            them in that order.
+// Activation columns of a batched GEMM chunk: kChunkTiles tiles, or half of
+// a single-chunk row that is split over two workgroups.
+inline constexpr int gemm_chunk_tiles(int ktiles, bool split) {
+  return ktiles > kChunkTiles ? kChunkTiles : (split ? ktiles / 2 : ktiles);
+}
+
 // Bits of Task::region.
 constexpr uint8_t kRegionLm = 1;      // weights are the LM head, not the arena
 constexpr uint8_t kRegionSplit = 2;   // batched: the block's chunks are split over two workgroups
@@ -135,7 +143,7 @@ struct Params {
   uint32_t* kvcur;       // [B][L][2][KVD] this step's bf16-rounded k, v
   uint32_t* o;           // [B][L][QD]  attention output
   uint32_t* h;           // [B][L][F]   SwiGLU hidden
-  uint32_t* kpart;       // [B][L][H]   second-half partial sums of split down tasks
+  uint32_t* kpart;       // [B][L][2][H] second-half partial sums of split O-proj / down tasks
   float* attn_part;      // [B][L][NKV][C][G*(D+2)] split-KV partials
   uint32_t* attn_ctr;    // [B][L][NKV][G] merge counters per head slice (epoch * C per step)
   uint64_t* amax;        // [B][num_wgs] argmax keys

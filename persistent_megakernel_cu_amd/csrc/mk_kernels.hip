@@ -1112,7 +1112,7 @@ __device__ __forceinline__ void loader_seek_b(const Params& P, Stream& st, int s
     if (op_is_gemv(t.op)) {
       const uint32_t n_items = (t.a1 - t.a0) << t.kslog;
       if ((uint32_t)wave < n_items) {
-        const uint32_t ch = t.nu < (uint32_t)kChunkTiles ? t.nu : (uint32_t)kChunkTiles;
+        const uint32_t ch = (uint32_t)gemm_chunk_tiles((int)t.nu, (t.region & kRegionSplit) != 0);
         st.ls = s;
         st.litem = (uint32_t)wave;
         st.lnitems = n_items;
@@ -1432,9 +1432,9 @@ __device__ __forceinline__ bool gemm_task(const Params& P, Ctx& c, Stream& st, c
   const int l = t.layer;
   const int stride = P.act_stride;
   float* rsb = c.red + 16;  // [kMaxBatch] RMSNorm scales of the sequences
-  const int kt = (int)t.nu, ch = kt < kChunkTiles ? kt : kChunkTiles, nc = kt / ch;
   // chunks [cb, ce) of every row: all, or one half of a block split over two workgroups
   const bool split = (t.region & kRegionSplit) != 0, half1 = (t.region & kRegionHalf1) != 0;
+  const int kt = (int)t.nu, ch = gemm_chunk_tiles(kt, split), nc = kt / ch;
   const int cb = half1 ? nc / 2 : 0, ce = split ? cb + nc / 2 : nc;
   const int ks = 1 << t.kslog, upc = ch >> t.kslog;
   const int nitems = (int)(t.a1 - t.a0) << t.kslog;
@@ -1489,7 +1489,7 @@ __device__ __forceinline__ bool gemm_task(const Params& P, Ctx& c, Stream& st, c
     const tword* src = OP == OP_OPROJ ? P.o + (size_t)l * P.QD : P.h + (size_t)l * P.F;
     const int kfull = OP == OP_OPROJ ? P.QD : P.F;
     const int col0 = cb * ch * kTileCols;
-    const int kc0 = min(ch * kTileCols, kfull - col0);
+    const int kc0 = max(0, min(ch * kTileCols, kfull - col0));  // 0: the half lies in the zero padding
     if (!stage_batch(P, c, c.act, stride, src, (size_t)P.L * kfull, col0, kc0, ch * kTileCols, s)) return false;
     if (c.flags[0]) return false;
     if (c.tid < P.B) rsb[c.tid] = 1.f;
@@ -1507,7 +1507,7 @@ __device__ __forceinline__ bool gemm_task(const Params& P, Ctx& c, Stream& st, c
     if (cc > cb) {  // next chunk of the activation (one item per wave: acc carries over)
       const tword* src = OP == OP_OPROJ ? P.o + (size_t)l * P.QD : P.h + (size_t)l * P.F;
       const int kfull = OP == OP_OPROJ ? P.QD : P.F;
-      const int kcc = min(ch * kTileCols, kfull - cc * ch * kTileCols);
+      const int kcc = max(0, min(ch * kTileCols, kfull - cc * ch * kTileCols));
       if (!stage_batch(P, c, c.act, stride, src, (size_t)P.L * kfull, cc * ch * kTileCols, kcc, ch * kTileCols, s))
         return false;
     }
@@ -1578,9 +1578,9 @@ __device__ __forceinline__ bool gemm_task(const Params& P, Ctx& c, Stream& st, c
           // reduced values back into the first part's tile for the argmax scan
           c.part[(size_t)(j * ks) * (kTileRows * 16) + q * 16 + n] = v * rsb[n];
           P.logits[(size_t)n * P.V + ((int)t.a0 + j) * kTileRows + q] = v * rsb[n];
-        } else if (OP == OP_DOWN && split) {
+        } else if (split) {
           // the second half hands its sums over; the first half adds them to its own
-          tword* kp = P.kpart + seq_off(P, n, l, P.H) + ((int)t.a0 + j) * kTileRows + q;
+          tword* kp = P.kpart + seq_off(P, n, l, 2 * P.H) + (OP == OP_DOWN ? P.H : 0) + ((int)t.a0 + j) * kTileRows + q;
           if (half1) {
             st_tag(kp, v, c.epoch);
             continue;
@@ -1600,7 +1600,7 @@ __device__ __forceinline__ bool gemm_task(const Params& P, Ctx& c, Stream& st, c
         }
       }
     }
-    if (OP == OP_DOWN && split) {  // a watchdog stop while waiting for the second half
+    if ((OP == OP_OPROJ || OP == OP_DOWN) && split) {  // a watchdog stop while waiting for the second half
       __syncthreads();
       if (c.flags[0]) return false;
     }

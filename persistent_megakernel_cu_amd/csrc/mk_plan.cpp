@@ -170,9 +170,12 @@ int plan_build(const mk_config& c, int W, Plan& p) {
     const uint64_t blocks = rows / kTileRows;
     const int nw = W - b0;
     const uint32_t ch = std::min<uint32_t>(ktiles, kChunkTiles);
-    const uint32_t nc = ktiles / ch;
-    if (op == OP_DOWN && b0 == 0 && 2 * blocks <= (uint64_t)W && nc >= 2 && nc % 2 == 0) {
+    const uint32_t sch = (uint32_t)gemm_chunk_tiles((int)ktiles, true);
+    const uint32_t snc = ktiles / sch;
+    if ((op == OP_DOWN || op == OP_OPROJ) && b0 == 0 && 2 * blocks <= (uint64_t)W && snc % 2 == 0 &&
+        sch % kWaves == 0 && ktiles % sch == 0) {
       // two workgroups per block, one per half of the row's chunks
+      const uint32_t ch = sch;
       uint32_t k = 0;
       while ((2u << k) <= (uint32_t)kWaves && (ch >> (k + 1)) > 0 && ch % (2u << k) == 0) ++k;
       for (uint64_t i = 0; i < 2 * blocks; ++i) {
@@ -344,7 +347,9 @@ int plan_validate(const Plan& p, std::string* why) {
         if (t.op != kind || t.layer != layer) return bad("stage holds another op");
         if (t.region & kRegionSplit) {
           // split block: the first half, then the second half on the next workgroup
-          if (kind != OP_DOWN || t.a1 != t.a0 + 1 || t.kslog == 0 || (kt / ch) % 2 != 0)
+          const uint64_t sch = (uint64_t)gemm_chunk_tiles((int)kt, true);
+          if ((kind != OP_DOWN && kind != OP_OPROJ) || t.a1 != t.a0 + 1 || t.kslog == 0 || kt % sch != 0 ||
+              (kt / sch) % 2 != 0 || sch % (1ull << t.kslog) != 0)
             return bad("split task geometry");
           if (!(t.region & kRegionHalf1)) {
             if (half0 >= 0 || t.a0 != next) return bad("split blocks not tiled exactly");
@@ -365,7 +370,7 @@ int plan_validate(const Plan& p, std::string* why) {
         if (t.ntasks != count) return bad("task count");
         if ((t.region & kRegionLm) != (kind == OP_LM ? kRegionLm : 0)) return bad("weight region");
         const uint64_t ks = 1ull << t.kslog, items = (uint64_t)(t.a1 - t.a0) * ks;
-        if (kt % ch != 0 || ch % ks != 0) return bad("parts do not divide the chunks");
+        if (kt % ch != 0 || (!(t.region & kRegionSplit) && ch % ks != 0)) return bad("parts do not divide the chunks");
         if (ks > 1 && items > (uint64_t)kWaves) return bad("split blocks need one item per wave");
         if (kt > ch && items > (uint64_t)kWaves) return bad("chunked rows need one item per wave");
         if ((kind == OP_OPROJ || kind == OP_DOWN) && (uint64_t)p.B * (t.a1 - t.a0) * kTileRows > (uint64_t)p.res_floats)
