@@ -35,9 +35,9 @@ HBM_PEAK_GBPS = 8000.0
 # commands are in profiles/mk_persistent_llama1b_hbm_bytes.md).  They describe
 # the kernel sources whose hash is recorded; any other source gives null.
 MEASURED_TRAFFIC = {
-    "sources_sha256_prefix": "916bce2858c7dd92",
-    "fetch_bytes": 2.5085e9,
-    "write_bytes": 6.14e6,
+    "sources_sha256_prefix": "e55f3f46032f1aa8",
+    "fetch_bytes": 2.5069e9,
+    "write_bytes": 6.151e6,
     "fetch_factor": 2.000,
     "write_factor": 1.000,
 }
