@@ -223,3 +223,39 @@ def test_llama1b_batch8_seeded_cache(llama1b):
     starts = [[make_start_token(LLAMA_1B, n)] for n in range(8)]
     run_batched_teacher_forced(LLAMA_1B, w, 1088, starts, 1024, 1, mode="mega", oracle_obj=o, kv_init=kv,
                                label="llama1b-b8")
+
+
+def test_tiny_free_running_matches_golden():
+    # Free-running greedy decode (each out_token is the next input) against the
+    # oracle's stored run (tests/golden/tiny_greedy.json): tokens must agree up
+    # to the first step whose top-2 margin is below the logit tolerance, where
+    # either token is acceptable and the runs may part.
+    import json
+    import os
+
+    with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "tiny_greedy.json")) as f:
+        gold = json.load(f)
+    w = make_weights(TINY, master=0, gain_jitter=0.1)
+    prompt = gold["prompt"]
+    gpu = GpuDecoder(TINY, w, len(prompt) + len(gold["steps"]) + 1, mode="mega")
+    try:
+        for p, t in enumerate(prompt):
+            lg, out = gpu.step(t, p)
+        pos = len(prompt)
+        compared = 0
+        for i, st in enumerate(gold["steps"]):
+            tol = 1e-2 * st["max_abs"]
+            for idx, val in st["top"]:
+                assert abs(float(lg[idx]) - val) <= tol, (i, idx, float(lg[idx]), val)
+            margin = st["top"][0][1] - st["top"][1][1]
+            if margin < tol:
+                break
+            assert out == gold["greedy_tokens"][i], (i, out, gold["greedy_tokens"][i])
+            compared += 1
+            if i + 1 < len(gold["steps"]):
+                lg, out = gpu.step(out, pos)
+                pos += 1
+        log(f"[golden] tiny free-running: {compared} tokens equal to the stored oracle run")
+        assert compared >= 4
+    finally:
+        gpu.close()
