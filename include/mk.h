@@ -209,9 +209,11 @@ int mk_trace_copy(mk_handle* h, uint64_t* out, int64_t capacity_words, int64_t* 
 /* mk_plan_describe -- build and validate the task tape for cfg on num_wgs
  * workgroups (0 = assume 256) on the HOST ONLY, without touching a GPU, and
  * fill *out.  Returns MK_OK if the tape passes the validator: stages in
- * dependency order, every row pair of every matrix covered exactly once,
- * every (kv head, chunk) attention task present once, LDS and scratch
- * bounds respected. */
+ * dependency order, every row pair of every matrix covered exactly once
+ * (in batched plans a 16-row block of the O- or down projection may be split
+ * over two workgroups by halves of its columns: then once per half, on
+ * neighbouring workgroups), every (kv head, chunk) attention task present
+ * once, LDS and scratch bounds respected. */
 int mk_plan_describe(const mk_config* cfg, int32_t num_wgs, mk_plan_info* out);
 
 #ifdef __cplusplus

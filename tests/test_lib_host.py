@@ -94,3 +94,38 @@ def test_null_arguments_are_rejected():
     assert L.mk_reset(None) == mkb.MK_E_INVAL
     assert L.mk_status(None, None) == mkb.MK_E_INVAL
     L.mk_free(None)
+
+
+def _batched_task_count(shape, max_seq, B, W=256):
+    """Tasks of a batched plan from the planner's rules: a GEMM stage of `blocks`
+    16-row blocks over nw workgroups has min(blocks, nw) tasks; an O- or down
+    projection with 2 * blocks <= W whose row (kt 32-column tiles) splits into an
+    even number of chunks of a multiple of 8 tiles (64-tile chunks, or two halves
+    of a single-chunk row) has two tasks per block; attention has one task per
+    (sequence, kv head, chunk); gate/up skips the attention workgroups when those
+    are at most an eighth of all."""
+    H, QD, KVD, F, V = shape.hidden, shape.q_dim, shape.kv_dim, shape.ffn, shape.vocab
+    pad = lambda x: (x + 511) // 512 * 512
+    C = min(-(-max_seq // 256), W // (B * shape.n_kv_heads))
+    seqs_kv = B * shape.n_kv_heads
+
+    def gemm(rows, kt, nw, splittable=False):
+        blocks = rows // 16
+        sch = 64 if kt > 64 else kt // 2
+        if splittable and 2 * blocks <= W and kt % sch == 0 and (kt // sch) % 2 == 0 and sch % 8 == 0:
+            return 2 * blocks
+        return min(blocks, nw)
+
+    gu_b0 = seqs_kv * C if seqs_kv * C * 8 <= W else 0
+    per_layer = (gemm(QD + 2 * KVD, pad(H) // 32, W) + seqs_kv * C + gemm(H, pad(QD) // 32, W, True)
+                 + gemm(2 * F, pad(H) // 32, W - gu_b0) + gemm(H, pad(F) // 32, W, True))
+    return shape.n_layers * per_layer + gemm(V, pad(H) // 32, W)
+
+
+@pytest.mark.parametrize("shape,max_seq,batch", [
+    (TINY, 48, 4), (TINY, 48, 8), (LLAMA_1B, 1088, 8), (LLAMA_1B, 256, 2)])
+def test_plan_batched_split_blocks(shape, max_seq, batch):
+    # O-proj and down blocks split over workgroup pairs where the rule allows
+    # (Llama-1B: 128 blocks each -> 256 tasks; tiny: 16 blocks -> 32 tasks)
+    info = mkb.plan_describe(shape, max_seq, 256, batch=batch)
+    assert info.num_tasks == _batched_task_count(shape, max_seq, batch)
