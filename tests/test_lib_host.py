@@ -129,3 +129,29 @@ def test_plan_batched_split_blocks(shape, max_seq, batch):
     # (Llama-1B: 128 blocks each -> 256 tasks; tiny: 16 blocks -> 32 tasks)
     info = mkb.plan_describe(shape, max_seq, 256, batch=batch)
     assert info.num_tasks == _batched_task_count(shape, max_seq, batch)
+
+
+def test_stage_timeline_summary():
+    # two layers (10 stages + LM head) on 4 workgroups with known stamps (kHz 1000 -> 1 tick = 1 us)
+    import numpy as np
+
+    from persistent_megakernel_cu_amd.timeline import stage_table
+
+    W, S = 4, 11
+    st = np.zeros((W, S, 20), dtype=np.uint64)
+    t = 100
+    for s in range(S):
+        for b in range(W):
+            # entered, ready = +2, done = +5 (+b for the stragglers), left = done
+            st[b, s, 0] = t
+            st[b, s, 1] = t + 2
+            st[b, s, 2] = t + 5 + b
+            st[b, s, 3] = t + 5 + b
+        t += 5 + W  # next stage starts after the slowest one
+    out = stage_table(st, 1000)
+    h, c, tl = out["per_kind"]["gate/up"]
+    # stage s starts at 100 + 9 s: ready +2, done +5..+8 over the workgroups (median +6.5)
+    assert abs(c - 4.5) < 1e-9                # median done - median ready
+    assert abs(tl - 1.5) < 1e-9               # latest done - median done
+    assert abs(h - 3.0) < 1e-9                # ready (+2) - previous stage's latest done (-9 + 8)
+    assert out["layers"] == 2 and out["rows"][0]["tasks"] == W
