@@ -74,6 +74,20 @@ def algorithmic_bytes(shape, pos: int, batch: int = 1) -> int:
     return w + kv_read + kv_write
 
 
+def cpu_model() -> str:
+    """Model name of the host CPU (first 'model name' line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
+
+
 def cpu_cores() -> int:
     for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS"):
         v = os.environ.get(var)
@@ -198,6 +212,7 @@ def cpu_baseline(wl, weights, budget_s: float = 12.0):
         "value": round(dt / n * 1e6, 1),
         "unit": "µs/token",
         "cores": cpu_cores(),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"{n} greedy decode step(s) of sequence 0 at positions {start_pos}..{start_pos + n - 1} over a "
                   f"cache whose first {filled} slots are seeded N(0,1) bf16 (for a prefilled prompt: the same "
@@ -292,11 +307,12 @@ def main() -> int:
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32 math, bf16 weights/KV, 24-bit activation words",
         "data": "synthetic",
         "config": {
             "workload": f"{wl.name}: batch-{B} greedy decode, {sh.name} shape ({model}), bf16 weights and KV "
-                        f"cache, fp32 activations and accumulation, {where}",
+                        f"cache, fp32 arithmetic and accumulation, activations handed between workgroups as 24-bit "
+                        f"words (the fp32 value rounded to 16 significant bits), {where}",
             "batch": B,
             "weights": "bf16 ~N(0,0.02) seed 0",
             "tokens_per_s": round(1e6 / us_tok, 1),

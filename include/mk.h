@@ -60,12 +60,15 @@ extern "C" {
  * key/value heads of head_dim each (n_heads % n_kv_heads == 0, head_dim even),
  * SwiGLU width ffn, vocabulary vocab.  max_seq bounds the positions and is
  * the slot count of the caller's KV cache; batch is the number of independent
- * sequences decoded per step (1 in this build).  rms_eps and rope_theta are
+ * sequences decoded per step (1..8; 2..8 run the GEMVs as skinny MFMA GEMMs
+ * and need head_dim 64).  rms_eps and rope_theta are
  * the RMSNorm epsilon and the RoPE base.  tie_embeddings != 0 uses the
  * embedding matrix as LM head.  exec_mode is one of MK_MODE_*.
  * attn_chunks: split of [0, pos] per KV head in attention (0 = automatic).
  * num_wgs: persistent workgroups (0 = one per compute unit).
- * watchdog_ms: budget of any single dependency wait (0 = 2000 ms).
+ * watchdog_ms: budget of any single dependency wait (0 = 2000 ms; a negative
+ * value is a budget of -watchdog_ms device clock ticks, which lets tests drive
+ * the timeout path with every workgroup still leaving the kernel normally).
  * trace: non-zero records, for every (workgroup, stage) of the latest step,
  * four device wall-clock stamps (see mk_trace_copy); off for timing runs. */
 typedef struct mk_config {
@@ -165,6 +168,13 @@ typedef struct mk_handle mk_handle;
 int mk_load(const mk_config* cfg, const mk_weights* w, mk_handle** out);
 
 /* mk_decode_step -- one decode step at position pos for every sequence.
+ * This is the forward pass the article runs as one kernel: per layer RMSNorm,
+ * the Q/K/V projections with the rotary embedding and the KV append, the
+ * attention over the cache, the output projection with its residual, the
+ * gated FFN with its residual, then the final norm, the LM head and the
+ * greedy token (article, the paragraphs on the Llama-1B forward pass as one
+ * kernel; glossary "Megakernel", "Wie eine ganze Rechenkette in ein Programm
+ * passt": the kernel runs the whole chain of operations of one token).
  * d_token[batch] (device int32) holds the input token ids; the previous
  * step's out_token may be passed directly.  kv is the caller's cache: slot
  * pos of every (sequence, layer, kv head) is written, slots [0, pos] are read,
@@ -181,7 +191,11 @@ int mk_decode_step(mk_handle* h, const int32_t* d_token, int32_t pos, const mk_k
 
 /* mk_reset -- wait for the handle's last stream, clear every flag, counter and
  * latched error and restart the step count.  Weights and the caller's cache
- * are untouched; a new sequence simply starts at pos = 0. */
+ * are untouched; a new sequence simply starts at pos = 0.  The plan built by
+ * mk_load is kept: the article's instruction sequences are planned once on
+ * the host and reused for every forward pass, so a new sequence only resets
+ * the dependency state the kernel keeps in device memory.
+ * Errors: MK_E_INVAL (null handle), MK_E_HIP. */
 int mk_reset(mk_handle* h);
 
 /* mk_free -- wait for outstanding work and release everything the handle owns. */

@@ -147,8 +147,11 @@ class Engine:
     """One mk_handle: weights loaded once, then one decode step per call.
 
     ``weights`` maps tensor names (see synth_inputs.weight_shapes) to device
-    tensors holding bf16 bit patterns (int16/uint16/bfloat16 dtype).  Only the
-    embedding must stay alive; the engine keeps a reference to it.
+    tensors holding bf16 bit patterns (int16/uint16/bfloat16 dtype).  The
+    library reads the embedding in place, and the LM head too (the embedding
+    when tied, else ``lm_head``) whenever the hidden size needs no row padding
+    (include/mk.h, mk_weights); the engine keeps a reference to the whole dict
+    so that no borrowed buffer is freed while the handle lives.
     """
 
     def __init__(self, shape, weights: dict, max_seq: int, mode: str = "mega", batch: int = 1,
@@ -168,7 +171,7 @@ class Engine:
         w.lm_head = weights["lm_head"].data_ptr() if not shape.tie_embeddings else None
         w.layers = layers
         del ptr
-        self._embed = weights["embed"]
+        self._weights = dict(weights)
         h = ctypes.c_void_p()
         rc = lib().mk_load(ctypes.byref(self.cfg), ctypes.byref(w), ctypes.byref(h))
         if rc != MK_OK:

@@ -2,8 +2,11 @@
 
     python -m persistent_megakernel_cu_amd.build
 
-hipcc cross-compiles for gfx950 without a GPU.  Packed-FP32 instruction
-selection is disabled for the device code.
+hipcc cross-compiles for gfx950 without a GPU.  Every translation unit is
+compiled to an object in _build/ (in parallel; the kernel instances are the
+builds of csrc/mk_inst.hip with their template parameters as defines), then
+linked into libmk.so.  Packed-FP32 instruction selection is disabled for the
+device code.
 """
 
 from __future__ import annotations
@@ -12,12 +15,22 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmk.so")
-SOURCES = ["mk_kernels.hip", "mk_api.cpp", "mk_plan.cpp"]
+OBJ_DIR = os.path.join(ROOT, "_build")
 ARCH = os.environ.get("MK_OFFLOAD_ARCH", "gfx950")
+
+# (object name, source, extra defines)
+INSTANCES = [(g, d, b) for (g, d, b) in
+             [(1, 64, 0), (2, 64, 0), (4, 64, 0), (1, 128, 0), (2, 128, 0), (4, 128, 0),
+              (1, 64, 1), (2, 64, 1), (4, 64, 1)]]
+UNITS = ([("mk_kernels", "mk_kernels.hip", []), ("mk_api", "mk_api.cpp", []), ("mk_plan", "mk_plan.cpp", [])]
+         + [(f"mk_inst_{g}_{d}_{b}", "mk_inst.hip", [f"-DMK_INST_G={g}", f"-DMK_INST_D={d}", f"-DMK_INST_B={b}"])
+            for (g, d, b) in INSTANCES])
 
 
 def hipcc() -> str:
@@ -27,26 +40,52 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (set HIPCC)")
 
 
+def common_flags() -> list[str]:
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wno-unused-command-line-argument", "-I", os.path.join(ROOT, "include")]
+
+
+def jobs() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
     """Compile every source into libmk.so; returns the library path."""
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    cc = hipcc()
+    extra = extra_flags or []
+
+    def compile_unit(u):
+        name, src, defs = u
+        obj = os.path.join(OBJ_DIR, name + ".o")
+        cmd = [cc] + common_flags() + defs + extra + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        return name, obj, cmd, r
+
+    with ThreadPoolExecutor(max_workers=jobs()) as ex:
+        results = list(ex.map(compile_unit, UNITS))
+    failed = False
+    for name, obj, cmd, r in results:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout + r.stderr)
+            failed = True
+    if failed:
+        raise RuntimeError("hipcc failed building libmk.so")
     tmp = LIB + ".tmp"
-    cmd = [
-        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-Wno-unused-command-line-argument",
-        "-I", os.path.join(os.path.dirname(PKG), "include"),
-        "-x", "hip",
-    ] + [os.path.join(CSRC, s) for s in SOURCES] + (extra_flags or []) + ["-o", tmp]
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + [obj for _, obj, _, _ in results]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building libmk.so")
-    if verbose and r.stderr.strip():
-        noise = [ln for ln in r.stderr.splitlines() if "packed-fp32-ops" not in ln and ln.strip()]
-        if noise:
-            sys.stderr.write("\n".join(noise) + "\n")
+        raise RuntimeError("hipcc failed linking libmk.so")
     os.replace(tmp, LIB)
     return LIB
 

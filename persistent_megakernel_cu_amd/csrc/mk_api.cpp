@@ -403,8 +403,13 @@ int mk_load(const mk_config* cfg, const mk_weights* w, mk_handle** out) {
   int wclk_khz = 0;
   HIP_OR(hipDeviceGetAttribute(&wclk_khz, hipDeviceAttributeWallClockRate, h->device));
   h->clock_khz = wclk_khz > 0 ? wclk_khz : 100000;
-  const uint64_t ms = cfg->watchdog_ms > 0 ? (uint64_t)cfg->watchdog_ms : 2000ull;
-  h->watchdog_ticks = (uint64_t)(wclk_khz > 0 ? wclk_khz : 100000) * ms;
+  if (cfg->watchdog_ms < 0) {
+    // a budget of -watchdog_ms device clock ticks: lets tests drive the timeout path
+    h->watchdog_ticks = (uint64_t)(-(int64_t)cfg->watchdog_ms);
+  } else {
+    const uint64_t ms = cfg->watchdog_ms > 0 ? (uint64_t)cfg->watchdog_ms : 2000ull;
+    h->watchdog_ticks = (uint64_t)(wclk_khz > 0 ? wclk_khz : 100000) * ms;
+  }
   HIP_OR(hipDeviceSynchronize());
   *out = h;
   return MK_OK;
@@ -469,12 +474,17 @@ int mk_decode_step(mk_handle* h, const int32_t* d_token, int32_t pos, const mk_k
 
 int mk_reset(mk_handle* h) {
   if (!h) return MK_E_INVAL;
-  if (hipDeviceSynchronize() != hipSuccess) {
+  // wait for the handle's own work only: the last stream a step ran on
+  if (h->used && hipStreamSynchronize(h->last_stream) != hipSuccess) {
     (void)hipGetLastError();
     return MK_E_HIP;
   }
-  if (hipMemset(h->ws, 0, h->wl.bytes) != hipSuccess) return MK_E_HIP;
-  if (hipDeviceSynchronize() != hipSuccess) return MK_E_HIP;
+  // the clear runs on the capture stream (never captured) and is waited for
+  if (hipMemsetAsync(h->ws, 0, h->wl.bytes, h->capture_stream) != hipSuccess ||
+      hipStreamSynchronize(h->capture_stream) != hipSuccess) {
+    (void)hipGetLastError();
+    return MK_E_HIP;
+  }
   std::memset(h->status_host, 0, sizeof(mk::DevStatus));
   h->epoch = 0;
   h->shadow_pos = -1;

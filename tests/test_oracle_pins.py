@@ -345,3 +345,47 @@ def test_cache_written_only_at_pos(tiny_weights):
     mask = np.ones(kc.shape, bool); mask[:, :, 4, :] = False
     np.testing.assert_array_equal(kc[mask], k0[mask])
     np.testing.assert_array_equal(vc[mask], v0[mask])
+
+
+# ---------------------------------------------------------------------------
+# Greedy token: first index of the maximum
+# ---------------------------------------------------------------------------
+
+
+def _first_max_scan(x):
+    """Left-to-right scan that replaces the best only on a strictly larger value."""
+    best, idx = x[0], 0
+    for i in range(1, len(x)):
+        if x[i] > best:
+            best, idx = x[i], i
+    return idx
+
+
+def test_argmax_first_ties_and_ends():
+    assert orc.argmax_first(np.array([1.0, 3.0, 3.0, 2.0], np.float32)) == 1
+    assert orc.argmax_first(np.array([1.0, 3.0, 3.0, 0.0], np.float32)) == 1
+    assert orc.argmax_first(np.full(17, -2.5, np.float32)) == 0          # all equal: the first
+    assert orc.argmax_first(np.array([5.0, 1.0, 5.0], np.float32)) == 0  # tie of the first and the last
+    assert orc.argmax_first(np.array([0.0, 1.0, 7.0], np.float32)) == 2  # maximum at the last index
+    assert orc.argmax_first(np.array([9.0, 1.0, 7.0], np.float32)) == 0  # maximum at the first index
+    # a signed value, not its magnitude, decides
+    assert orc.argmax_first(np.array([-10.0, 2.0, -3.0], np.float32)) == 1
+    # -0.0 and +0.0 compare equal: the first of them wins
+    assert orc.argmax_first(np.array([-1.0, -0.0, 0.0], np.float32)) == 1
+    assert orc.argmax_first(np.array([-1.0, 0.0, -0.0], np.float32)) == 1
+
+
+def test_argmax_first_matches_scan_on_random_ties():
+    # values from a small set, so many ties at the maximum, checked against a scalar scan
+    rng = np.random.default_rng(13)
+    for _ in range(200):
+        n = int(rng.integers(1, 64))
+        x = rng.integers(-3, 4, n).astype(np.float32)
+        assert orc.argmax_first(x) == _first_max_scan(x)
+
+
+@pytest.mark.parametrize("bad", [np.nan, np.inf, -np.inf])
+def test_argmax_first_rejects_non_finite(bad):
+    x = np.array([0.0, 1.0, bad, 2.0], np.float32)
+    with pytest.raises(AssertionError):
+        orc.argmax_first(x)
