@@ -1,7 +1,9 @@
 #!/usr/bin/env python3
 """Decode benchmark: us/token of greedy decode on one MI355X, with the
 achieved HBM bandwidth of the megakernel against the 8 TB/s peak, the
-launch-per-stage and hipGraph baselines, and the CPU oracle.
+baselines (the conventional one-kernel-per-operation path, eager and captured
+in a hipGraph; the megakernel's own executors launched once per stage, eager
+and captured) and the CPU oracle.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
@@ -241,7 +243,10 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=128)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="llama1b")
-    ap.add_argument("--modes", default="mega,graph,multi")
+    ap.add_argument("--modes", default="mega,graph,multi,conv,conv-graph",
+                    help="mega: the persistent megakernel; graph / multi: its executors one launch per stage, "
+                         "captured or not; conv / conv-graph: the conventional one-kernel-per-operation path, "
+                         "eager or captured in a hipGraph")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--attn-chunks", type=int, default=0, help="KV split per head (0: automatic)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -336,6 +341,8 @@ def main() -> int:
         out["per_position_us"] = {str(p): round(t * 1e3, 2) for p, t in sorted(per_pos[main_mode].items())}
     if "graph" in results and "mega" in results:
         out["speedup_vs_graph"] = round(results["graph"] / results["mega"], 3)
+    if "conv-graph" in results and "mega" in results:
+        out["speedup_vs_conv_graph"] = round(results["conv-graph"] / results["mega"], 3)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(wl, weights)
     print(json.dumps(out), flush=True)

@@ -31,6 +31,7 @@
 #ifndef MK_H_
 #define MK_H_
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -51,9 +52,12 @@ extern "C" {
 #define MK_E_DEVICE (-9)      /* device does not fit the persistent launch         */
 
 /* Execution modes of mk_decode_step. */
-#define MK_MODE_MEGA 0  /* one persistent kernel per decode step                 */
-#define MK_MODE_MULTI 1 /* one kernel launch per stage (the bubble baseline)     */
-#define MK_MODE_GRAPH 2 /* the MULTI launches captured once into a hipGraph      */
+#define MK_MODE_MEGA 0       /* one persistent kernel per decode step                        */
+#define MK_MODE_MULTI 1      /* the megakernel's executors, one launch per stage             */
+#define MK_MODE_GRAPH 2      /* the MULTI launches captured once into a hipGraph             */
+#define MK_MODE_CONV 3       /* conventional path: one plain kernel per operation (see
+                                mk_conv_decode_step), the bubble baseline                    */
+#define MK_MODE_CONV_GRAPH 4 /* the MK_MODE_CONV launches captured once into a hipGraph      */
 
 /* Model and run configuration.
  * Llama-style decoder: n_layers, hidden H, n_heads query heads and n_kv_heads
@@ -229,6 +233,54 @@ int mk_trace_copy(mk_handle* h, uint64_t* out, int64_t capacity_words, int64_t* 
  * neighbouring workgroups), every (kv head, chunk) attention task present
  * once, LDS and scratch bounds respected. */
 int mk_plan_describe(const mk_config* cfg, int32_t num_wgs, mk_plan_info* out);
+
+/* ---------------------------------------------------------------------------
+ * The conventional path: one plain kernel launch per operation.
+ *
+ * The article's paragraphs on the typical challenges of decode and on mid-size
+ * models, and the glossary entry "Megakernel", section "Warum die Pausen
+ * zwischen den Rechenschritten teuer sind", describe the usual execution that
+ * the megakernel replaces: the forward pass as a long series of short kernels,
+ * each started separately, with idle gaps between them that streams and
+ * graphs shorten but do not remove.  These calls run that usual execution on
+ * the same weights and cache layout, with kernels that share nothing with the
+ * megakernel: per layer RMSNorm, the Q, K and V GEMVs, RoPE + KV append,
+ * split-KV attention and its merge, O projection + residual, RMSNorm, the
+ * gate and up GEMVs, SiLU product, down projection + residual; then the final
+ * RMSNorm, the LM head and a two-kernel argmax (4 + 13 * n_layers launches).
+ * Activations are fp32.  The handle modes MK_MODE_CONV and MK_MODE_CONV_GRAPH
+ * run it through mk_load / mk_decode_step; a caller can also capture one call
+ * into its own hipGraph: every launch is a kernel and the position is read
+ * from device memory.
+ * ------------------------------------------------------------------------- */
+
+/* mk_conv_workspace_size -- bytes of the fp32 workspace one conventional step
+ * needs for cfg (activations, attention partials, argmax partials).  Only the
+ * model dimensions, max_seq and batch (1..8) of cfg are used.
+ * Errors: MK_E_INVAL (null, or dimensions that are not positive, head_dim,
+ * hidden or ffn not multiples of 8, n_heads not a multiple of n_kv_heads),
+ * MK_E_UNSUPPORTED (head_dim above 128 or not 8 times a power of two, batch
+ * above 8). */
+int mk_conv_workspace_size(const mk_config* cfg, size_t* bytes);
+
+/* mk_conv_decode_step -- one decode step of cfg.batch sequences with the
+ * conventional path, asynchronous on stream.
+ * w: the caller's weights (device pointers, read in place; every matrix and
+ * the LM head 16-byte aligned; the host array w->layers is read during the
+ * call only).  d_token[batch] (device int32): input tokens.  d_pos (device
+ * int32): the position, in [0, max_seq) (a position outside it makes every
+ * kernel return without writing the cache).  kv: the caller's bf16 cache as in
+ * mk_decode_step (16-byte aligned); slot pos is written, [0, pos] read.
+ * out_logits[batch][vocab] (device fp32) and out_token[batch] (device int32,
+ * first index of the maximum; -1 for an input token outside [0, vocab)) are
+ * written.  workspace: device memory of at least mk_conv_workspace_size
+ * bytes, 256-byte aligned, owned by the caller and not used by any other
+ * work until the step has run.  Allocates nothing, never synchronises.
+ * Errors: those of mk_conv_workspace_size, MK_E_INVAL (null or misaligned
+ * pointers, workspace too small), MK_E_HIP (a launch failed). */
+int mk_conv_decode_step(const mk_config* cfg, const mk_weights* w, const int32_t* d_token, const int32_t* d_pos,
+                        const mk_kv* kv, float* out_logits, int32_t* out_token, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

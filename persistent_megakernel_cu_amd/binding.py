@@ -32,7 +32,10 @@ TRACE_STAMPS = 20  # stamps per (workgroup, stage) trace record
 MODE_MEGA = 0
 MODE_MULTI = 1
 MODE_GRAPH = 2
-MODES = {"mega": MODE_MEGA, "multi": MODE_MULTI, "graph": MODE_GRAPH}
+MODE_CONV = 3
+MODE_CONV_GRAPH = 4
+MODES = {"mega": MODE_MEGA, "multi": MODE_MULTI, "graph": MODE_GRAPH, "conv": MODE_CONV,
+         "conv-graph": MODE_CONV_GRAPH}
 
 
 class MkConfig(ctypes.Structure):
@@ -106,6 +109,12 @@ def lib() -> ctypes.CDLL:
         L.mk_trace_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64),
                                     ctypes.POINTER(ctypes.c_int32)]
         L.mk_trace_copy.restype = ctypes.c_int
+        L.mk_conv_workspace_size.argtypes = [ctypes.POINTER(MkConfig), ctypes.POINTER(ctypes.c_size_t)]
+        L.mk_conv_workspace_size.restype = ctypes.c_int
+        L.mk_conv_decode_step.argtypes = [ctypes.POINTER(MkConfig), ctypes.POINTER(MkWeights), ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.POINTER(MkKv), ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.mk_conv_decode_step.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -143,6 +152,54 @@ def plan_describe(shape, max_seq: int, num_wgs: int = 256, **kw) -> MkPlanInfo:
     return info
 
 
+def weights_struct(shape, weights: dict):
+    """(MkWeights, layer array) pointing at the device tensors of ``weights``;
+    keep both (and the tensors) alive while the library may read them."""
+    layers = (MkLayerWeights * max(1, shape.n_layers))()
+    for l in range(shape.n_layers):
+        for f in MkLayerWeights._fields_:
+            setattr(layers[l], f[0], weights[f"layers.{l}.{f[0]}"].data_ptr())
+    w = MkWeights()
+    w.embed = weights["embed"].data_ptr()
+    w.final_norm = weights["final_norm"].data_ptr()
+    w.lm_head = weights["lm_head"].data_ptr() if not shape.tie_embeddings else None
+    w.layers = layers
+    return w, layers
+
+
+def _stream_handle(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def conv_workspace_size(shape, max_seq: int, batch: int = 1) -> int:
+    """Bytes of the conventional path's workspace (mk_conv_workspace_size; no GPU needed)."""
+    n = ctypes.c_size_t()
+    rc = lib().mk_conv_workspace_size(ctypes.byref(make_config(shape, max_seq, batch)), ctypes.byref(n))
+    if rc != MK_OK:
+        raise MkError(rc, "mk_conv_workspace_size")
+    return n.value
+
+
+def conv_decode_step(shape, weights: dict, max_seq: int, token, d_pos, kcache, vcache, logits, out_token,
+                     workspace, batch: int = 1, stream=None) -> None:
+    """One conventional step through mk_conv_decode_step (stateless; d_pos is a
+    device int32 tensor, workspace a device buffer of conv_workspace_size bytes)."""
+    cfg = make_config(shape, max_seq, batch)
+    w, layers = weights_struct(shape, weights)
+    kv = MkKv()
+    kv.k, kv.v = kcache.data_ptr(), vcache.data_ptr()
+    rc = lib().mk_conv_decode_step(ctypes.byref(cfg), ctypes.byref(w), token.data_ptr(), d_pos.data_ptr(),
+                                   ctypes.byref(kv), logits.data_ptr(), out_token.data_ptr(), workspace.data_ptr(),
+                                   workspace.numel() * workspace.element_size(),
+                                   ctypes.c_void_p(_stream_handle(stream)))
+    del layers
+    if rc != MK_OK:
+        raise MkError(rc, "mk_conv_decode_step")
+
+
 class Engine:
     """One mk_handle: weights loaded once, then one decode step per call.
 
@@ -160,17 +217,7 @@ class Engine:
         self.max_seq = max_seq
         self.batch = batch
         self.cfg = make_config(shape, max_seq, batch, mode, attn_chunks, num_wgs, watchdog_ms, trace)
-        ptr = lambda name: ctypes.c_void_p(weights[name].data_ptr())
-        layers = (MkLayerWeights * max(1, shape.n_layers))()
-        for l in range(shape.n_layers):
-            for f in MkLayerWeights._fields_:
-                setattr(layers[l], f[0], weights[f"layers.{l}.{f[0]}"].data_ptr())
-        w = MkWeights()
-        w.embed = weights["embed"].data_ptr()
-        w.final_norm = weights["final_norm"].data_ptr()
-        w.lm_head = weights["lm_head"].data_ptr() if not shape.tie_embeddings else None
-        w.layers = layers
-        del ptr
+        w, layers = weights_struct(shape, weights)
         self._weights = dict(weights)
         h = ctypes.c_void_p()
         rc = lib().mk_load(ctypes.byref(self.cfg), ctypes.byref(w), ctypes.byref(h))
@@ -181,11 +228,7 @@ class Engine:
 
     def decode_step(self, token, pos: int, kcache, vcache, logits, out_token, stream=None) -> None:
         """Enqueue one step on ``stream`` (a torch.cuda.Stream or raw handle; default: current)."""
-        if stream is None:
-            import torch
-            stream = torch.cuda.current_stream().cuda_stream
-        elif hasattr(stream, "cuda_stream"):
-            stream = stream.cuda_stream
+        stream = _stream_handle(stream)
         self._kv.k = kcache.data_ptr()
         self._kv.v = vcache.data_ptr()
         rc = lib().mk_decode_step(self._h, token.data_ptr(), int(pos), ctypes.byref(self._kv), logits.data_ptr(),

@@ -20,6 +20,8 @@ hipError_t launch_persistent(const Params& P, int lds_bytes, hipStream_t stream)
 hipError_t launch_stage(const Params& P, int s, int lds_bytes, hipStream_t stream);
 hipError_t launch_set_args(StepArgs* a, int pos, uint32_t epoch, hipStream_t stream);
 hipError_t launch_advance_args(StepArgs* a, hipStream_t stream);
+hipError_t conv_launch_set_pos(int32_t* d_pos, int pos, hipStream_t s);
+hipError_t conv_launch_advance_pos(int32_t* d_pos, hipStream_t s);
 }  // namespace mk
 
 using mk::Params;
@@ -94,6 +96,13 @@ struct mk_handle {
   const void* g_ptrs[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
   int shadow_pos = -1;
   uint32_t shadow_epoch = 0;
+  // conventional modes: the caller's weights (layers copied), fp32 workspace, device position
+  bool conv = false;
+  mk_weights conv_w{};
+  std::vector<mk_layer_weights> conv_layers;
+  char* conv_ws = nullptr;
+  size_t conv_ws_bytes = 0;
+  int32_t* conv_pos = nullptr;
 };
 
 namespace {
@@ -110,6 +119,8 @@ void release(mk_handle* h) {
   if (h->tape) (void)hipFree(h->tape);
   if (h->ws) (void)hipFree(h->ws);
   if (h->trace) (void)hipFree(h->trace);
+  if (h->conv_ws) (void)hipFree(h->conv_ws);
+  if (h->conv_pos) (void)hipFree(h->conv_pos);
   if (h->status_host) (void)hipHostFree(h->status_host);
   delete h;
 }
@@ -216,6 +227,90 @@ int capture_graph(mk_handle* h, const Params& base) {
   return MK_OK;
 }
 
+// Conventional hipGraph mode: one step of per-operation launches plus the
+// position advance, captured once and replayed.
+int capture_conv_graph(mk_handle* h, const int32_t* d_token, const mk_kv* kv, float* logits, int32_t* tok) {
+  if (h->gexec) { (void)hipGraphExecDestroy(h->gexec); h->gexec = nullptr; }
+  if (h->graph) { (void)hipGraphDestroy(h->graph); h->graph = nullptr; }
+  hipStream_t cs = h->capture_stream;
+  if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) return MK_E_HIP;
+  int rc = mk_conv_decode_step(&h->cfg, &h->conv_w, d_token, h->conv_pos, kv, logits, tok, h->conv_ws,
+                               h->conv_ws_bytes, cs);
+  bool ok = rc == MK_OK && mk::conv_launch_advance_pos(h->conv_pos, cs) == hipSuccess;
+  hipGraph_t g = nullptr;
+  hipError_t e = hipStreamEndCapture(cs, &g);
+  if (!ok || e != hipSuccess || !g) {
+    if (g) (void)hipGraphDestroy(g);
+    (void)hipGetLastError();
+    return rc != MK_OK ? rc : MK_E_HIP;
+  }
+  if (hipGraphInstantiate(&h->gexec, g, nullptr, nullptr, 0) != hipSuccess) {
+    (void)hipGraphDestroy(g);
+    h->gexec = nullptr;
+    return MK_E_HIP;
+  }
+  h->graph = g;
+  h->shadow_pos = -1;
+  return MK_OK;
+}
+
+// mk_load for MK_MODE_CONV / MK_MODE_CONV_GRAPH: no plan and no repack; the
+// caller's weights are read in place by the per-operation kernels.
+int load_conv(const mk_config* cfg, const mk_weights* w, mk_handle** out) {
+  size_t bytes = 0;
+  int rc = mk_conv_workspace_size(cfg, &bytes);
+  if (rc != MK_OK) return rc;
+  if (!w->embed || !w->final_norm || (cfg->n_layers > 0 && !w->layers)) return MK_E_INVAL;
+  mk_handle* h = new (std::nothrow) mk_handle();
+  if (!h) return MK_E_NOMEM;
+  h->cfg = *cfg;
+  h->conv = true;
+  h->conv_layers.assign(w->layers, w->layers + cfg->n_layers);
+  h->conv_w = *w;
+  h->conv_w.layers = h->conv_layers.data();
+  HIP_OR(hipGetDevice(&h->device));
+  if (hipMalloc(&h->conv_ws, bytes) != hipSuccess) { (void)hipGetLastError(); release(h); return MK_E_NOMEM; }
+  h->conv_ws_bytes = bytes;
+  HIP_OR(hipMalloc(&h->conv_pos, 256));
+  HIP_OR(hipMemset(h->conv_pos, 0, 256));
+  HIP_OR(hipHostMalloc(reinterpret_cast<void**>(&h->status_host), sizeof(mk::DevStatus), hipHostMallocMapped));
+  std::memset(h->status_host, 0, sizeof(mk::DevStatus));
+  HIP_OR(hipStreamCreateWithFlags(&h->capture_stream, hipStreamNonBlocking));
+  HIP_OR(hipDeviceSynchronize());
+  *out = h;
+  return MK_OK;
+}
+
+int decode_conv(mk_handle* h, const int32_t* d_token, int32_t pos, const mk_kv* kv, float* logits, int32_t* tok,
+                hipStream_t stream) {
+  if (pos < 0 || pos >= h->cfg.max_seq) return MK_E_RANGE;
+  int rc = MK_OK;
+  if (h->cfg.exec_mode == MK_MODE_CONV) {
+    if (mk::conv_launch_set_pos(h->conv_pos, pos, stream) != hipSuccess) return MK_E_HIP;
+    rc = mk_conv_decode_step(&h->cfg, &h->conv_w, d_token, h->conv_pos, kv, logits, tok, h->conv_ws,
+                             h->conv_ws_bytes, stream);
+  } else {
+    const void* ptrs[5] = {d_token, kv->k, kv->v, logits, tok};
+    if (!h->gexec || std::memcmp(ptrs, h->g_ptrs, sizeof(ptrs)) != 0) {
+      if ((rc = capture_conv_graph(h, d_token, kv, logits, tok)) != MK_OK) return rc;
+      std::memcpy(h->g_ptrs, ptrs, sizeof(ptrs));
+    }
+    hipError_t e = hipSuccess;
+    if (h->shadow_pos != pos) e = mk::conv_launch_set_pos(h->conv_pos, pos, stream);
+    if (e == hipSuccess) e = hipGraphLaunch(h->gexec, stream);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return MK_E_HIP;
+    }
+    h->shadow_pos = pos + 1;
+  }
+  if (rc == MK_OK) {
+    h->last_stream = stream;
+    h->used = true;
+  }
+  return rc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -258,6 +353,7 @@ int mk_plan_describe(const mk_config* cfg, int32_t num_wgs, mk_plan_info* out) {
 int mk_load(const mk_config* cfg, const mk_weights* w, mk_handle** out) {
   if (out) *out = nullptr;
   if (!cfg || !w || !out || !w->embed || !w->final_norm) return MK_E_INVAL;
+  if (cfg->exec_mode == MK_MODE_CONV || cfg->exec_mode == MK_MODE_CONV_GRAPH) return load_conv(cfg, w, out);
   if ((cfg->tie_embeddings != 0) != (w->lm_head == nullptr)) return MK_E_INVAL;
   if (cfg->n_layers > 0 && !w->layers) return MK_E_INVAL;
   for (int l = 0; l < cfg->n_layers; ++l) {
@@ -423,6 +519,7 @@ int mk_decode_step(mk_handle* h, const int32_t* d_token, int32_t pos, const mk_k
   if ((reinterpret_cast<uintptr_t>(out_logits) | reinterpret_cast<uintptr_t>(out_token) |
        reinterpret_cast<uintptr_t>(d_token)) & 3u)
     return MK_E_INVAL;
+  if (h->conv) return decode_conv(h, d_token, pos, kv, out_logits, out_token, stream);
   if (pos < 0 || pos >= h->plan.S) return MK_E_RANGE;
   if (reinterpret_cast<volatile int32_t*>(&h->status_host->code)[0] != MK_OK) return MK_E_STATE;
   if (h->epoch + 1 >= kEpochLimit) {
@@ -478,6 +575,10 @@ int mk_reset(mk_handle* h) {
   if (h->used && hipStreamSynchronize(h->last_stream) != hipSuccess) {
     (void)hipGetLastError();
     return MK_E_HIP;
+  }
+  if (h->conv) {  // no dependency state: the workspace is rewritten by every step
+    h->shadow_pos = -1;
+    return MK_OK;
   }
   // the clear runs on the capture stream (never captured) and is waited for
   if (hipMemsetAsync(h->ws, 0, h->wl.bytes, h->capture_stream) != hipSuccess ||

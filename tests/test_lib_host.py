@@ -12,7 +12,7 @@ from synth_inputs import LLAMA_1B, LLAMA_8B, TINY
 def test_exports_every_declared_function():
     names = mkb.header_functions()
     assert set(names) == {"mk_load", "mk_decode_step", "mk_reset", "mk_free", "mk_status", "mk_error_string",
-                          "mk_plan_describe", "mk_trace_copy"}
+                          "mk_plan_describe", "mk_trace_copy", "mk_conv_workspace_size", "mk_conv_decode_step"}
     L = mkb.lib()
     for n in names:
         assert getattr(L, n) is not None
@@ -155,3 +155,30 @@ def test_stage_timeline_summary():
     assert abs(tl - 1.5) < 1e-9               # latest done - median done
     assert abs(h - 3.0) < 1e-9                # ready (+2) - previous stage's latest done (-9 + 8)
     assert out["layers"] == 2 and out["rows"][0]["tasks"] == W
+
+
+def test_conv_workspace_size():
+    # fp32 activations (x, xn, q, k, v, attention out, gate, up, hid), split-KV
+    # partials of 256-position chunks and the argmax keys, 256-byte aligned pieces
+    sh = TINY
+    H, QD, KVD, F = sh.hidden, sh.q_dim, sh.kv_dim, sh.ffn
+    up = lambda n: (n + 255) // 256 * 256
+    for B, S in ((1, 48), (3, 600)):
+        C = -(-S // 256)
+        want = (up(B * H * 4) * 2 + up(B * QD * 4) * 2 + up(B * KVD * 4) * 2 + up(B * F * 4) * 3
+                + up(B * sh.n_heads * C * (sh.head_dim + 2) * 4) + up(B * 256 * 8) + up(B * 4))
+        assert mkb.conv_workspace_size(sh, S, B) == want
+
+
+def test_conv_rejects_bad_configs():
+    for kw, code in ((dict(head_dim=24), mkb.MK_E_UNSUPPORTED), (dict(head_dim=256), mkb.MK_E_UNSUPPORTED),
+                     (dict(hidden=260), mkb.MK_E_INVAL), (dict(n_heads=3), mkb.MK_E_INVAL)):
+        with pytest.raises(mkb.MkError) as e:
+            mkb.conv_workspace_size(TINY.with_(**kw), 48)
+        assert e.value.code == code
+    with pytest.raises(mkb.MkError) as e:
+        mkb.conv_workspace_size(TINY, 48, 9)
+    assert e.value.code == mkb.MK_E_UNSUPPORTED
+    n = ctypes.c_size_t()
+    assert mkb.lib().mk_conv_workspace_size(None, ctypes.byref(n)) == mkb.MK_E_INVAL
+    assert mkb.lib().mk_conv_decode_step(None, None, None, None, None, None, None, None, 0, None) == mkb.MK_E_INVAL
