@@ -50,6 +50,7 @@ extern "C" {
 #define MK_E_NOMEM (-7)       /* device or host allocation failed                  */
 #define MK_E_UNSUPPORTED (-8) /* configuration not supported by this build         */
 #define MK_E_DEVICE (-9)      /* device does not fit the persistent launch         */
+#define MK_E_TOOBIG (-10)     /* the step needs more than the fixed static scratch  */
 
 /* Execution modes of mk_decode_step. */
 #define MK_MODE_MEGA 0       /* one persistent kernel per decode step                        */
@@ -281,6 +282,22 @@ int mk_conv_workspace_size(const mk_config* cfg, size_t* bytes);
 int mk_conv_decode_step(const mk_config* cfg, const mk_weights* w, const int32_t* d_token, const int32_t* d_pos,
                         const mk_kv* kv, float* out_logits, int32_t* out_token, void* workspace,
                         size_t workspace_bytes, hipStream_t stream);
+
+/* mk_conv_decode_step_static -- mk_conv_decode_step for callers that cannot
+ * allocate device memory at all (code under hipGraph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the workspace is a fixed buffer of
+ * 8 MiB in the library's static device memory, one per GPU, looked up on the
+ * first call made on that GPU (enough for the Llama-1B shape at batch 8 over
+ * 8192 positions; compare mk_conv_workspace_size).  The
+ * caller still passes inputs and outputs; arguments and results are exactly
+ * those of mk_conv_decode_step.  Calls on one GPU share that buffer: calls
+ * that overlap in time on one GPU (other streams, other threads) race and must
+ * be serialised by the caller.  Allocates nothing, never synchronises.
+ * Errors: those of mk_conv_decode_step, MK_E_TOOBIG (the configuration needs a
+ * workspace larger than the buffer; see mk_conv_workspace_size), MK_E_HIP. */
+int mk_conv_decode_step_static(const mk_config* cfg, const mk_weights* w, const int32_t* d_token,
+                               const int32_t* d_pos, const mk_kv* kv, float* out_logits, int32_t* out_token,
+                               hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -26,6 +26,7 @@ MK_E_TOKEN = -6
 MK_E_NOMEM = -7
 MK_E_UNSUPPORTED = -8
 MK_E_DEVICE = -9
+MK_E_TOOBIG = -10
 
 TRACE_STAMPS = 20  # stamps per (workgroup, stage) trace record
 
@@ -115,6 +116,10 @@ def lib() -> ctypes.CDLL:
                                           ctypes.c_void_p, ctypes.POINTER(MkKv), ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         L.mk_conv_decode_step.restype = ctypes.c_int
+        L.mk_conv_decode_step_static.argtypes = [ctypes.POINTER(MkConfig), ctypes.POINTER(MkWeights),
+                                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(MkKv),
+                                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.mk_conv_decode_step_static.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -198,6 +203,22 @@ def conv_decode_step(shape, weights: dict, max_seq: int, token, d_pos, kcache, v
     del layers
     if rc != MK_OK:
         raise MkError(rc, "mk_conv_decode_step")
+
+
+def conv_decode_step_static(shape, weights: dict, max_seq: int, token, d_pos, kcache, vcache, logits, out_token,
+                            batch: int = 1, stream=None) -> None:
+    """One conventional step through mk_conv_decode_step_static (the library's
+    fixed per-GPU scratch instead of a caller workspace)."""
+    cfg = make_config(shape, max_seq, batch)
+    w, layers = weights_struct(shape, weights)
+    kv = MkKv()
+    kv.k, kv.v = kcache.data_ptr(), vcache.data_ptr()
+    rc = lib().mk_conv_decode_step_static(ctypes.byref(cfg), ctypes.byref(w), token.data_ptr(), d_pos.data_ptr(),
+                                          ctypes.byref(kv), logits.data_ptr(), out_token.data_ptr(),
+                                          ctypes.c_void_p(_stream_handle(stream)))
+    del layers
+    if rc != MK_OK:
+        raise MkError(rc, "mk_conv_decode_step_static")
 
 
 class Engine:

@@ -538,6 +538,43 @@ int check_step_args(const Dims& d, const int32_t* d_token, const int32_t* d_pos,
   return MK_OK;
 }
 
+// ---------------------------------------------------------------------------
+// the allocation-free variant: a fixed device buffer instead of a workspace
+// ---------------------------------------------------------------------------
+
+// Workspace of mk_conv_decode_step_static.  Each GPU the library runs on holds
+// its own copy until the process ends.  In host code this name is only a
+// stand-in for the symbol: the device address of a GPU's copy comes from
+// hipGetSymbolAddress with that GPU current (static_scratch below), and only
+// that address is ever handed to a kernel.
+constexpr size_t kStaticScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current GPU's scratch, looked up once per device.
+int static_scratch(char** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return MK_E_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return MK_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return MK_E_HIP;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = static_cast<char*>(g_scratch_ptr[dev]);
+  return MK_OK;
+}
+
 }  // namespace mkconv
 
 // ---------------------------------------------------------------------------
@@ -576,6 +613,22 @@ int mk_conv_decode_step(const mk_config* cfg, const mk_weights* w, const int32_t
   if ((rc = mkconv::check_step_args(d, d_token, d_pos, kv, out_logits, out_token)) != MK_OK) return rc;
   if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < mkconv::layout_of(d).bytes) return MK_E_INVAL;
   return mkconv::run_step(d, w, d_token, d_pos, kv, out_logits, out_token, static_cast<char*>(workspace), stream);
+}
+
+int mk_conv_decode_step_static(const mk_config* cfg, const mk_weights* w, const int32_t* d_token,
+                               const int32_t* d_pos, const mk_kv* kv, float* out_logits, int32_t* out_token,
+                               hipStream_t stream) {
+  mkconv::Dims d{};
+  int rc = mkconv::dims_of(cfg, &d);
+  if (rc != MK_OK) return rc;
+  if ((rc = mkconv::check_weights(d, w)) != MK_OK) return rc;
+  if ((rc = mkconv::check_step_args(d, d_token, d_pos, kv, out_logits, out_token)) != MK_OK) return rc;
+  if (mkconv::layout_of(d).bytes > mkconv::kStaticScratchBytes) return MK_E_TOOBIG;
+  char* ws = nullptr;
+  if ((rc = mkconv::static_scratch(&ws)) != MK_OK) return rc;
+  // every workspace element a step reads was written earlier in the same
+  // step, so nothing left by a previous call needs clearing
+  return mkconv::run_step(d, w, d_token, d_pos, kv, out_logits, out_token, ws, stream);
 }
 
 }  // extern "C"

@@ -327,6 +327,7 @@ const char* mk_error_string(int code) {
     case MK_E_NOMEM: return "out of memory";
     case MK_E_UNSUPPORTED: return "configuration not supported";
     case MK_E_DEVICE: return "device cannot host the persistent launch";
+    case MK_E_TOOBIG: return "the step needs a larger workspace than the static scratch buffer";
     default: return "unknown error";
   }
 }

@@ -12,14 +12,15 @@ from synth_inputs import LLAMA_1B, LLAMA_8B, TINY
 def test_exports_every_declared_function():
     names = mkb.header_functions()
     assert set(names) == {"mk_load", "mk_decode_step", "mk_reset", "mk_free", "mk_status", "mk_error_string",
-                          "mk_plan_describe", "mk_trace_copy", "mk_conv_workspace_size", "mk_conv_decode_step"}
+                          "mk_plan_describe", "mk_trace_copy", "mk_conv_workspace_size", "mk_conv_decode_step",
+                          "mk_conv_decode_step_static"}
     L = mkb.lib()
     for n in names:
         assert getattr(L, n) is not None
 
 
 def test_error_strings():
-    for code in range(0, -10, -1):
+    for code in range(0, -11, -1):
         assert mkb.error_string(code) and mkb.error_string(code) != "unknown error"
     assert mkb.error_string(-99) == "unknown error"
 
