@@ -128,7 +128,8 @@ def time_mode(mk, torch, wl, wdev, mode, warmup, steps, max_seq, attn_chunks=0):
     from synth_inputs import make_prompt, make_start_token
 
     shape, B = wl.shape, wl.batch
-    eng = mk.Engine(shape, wdev, max_seq, mode=mode, batch=B, attn_chunks=attn_chunks)
+    exec_mode, partial = (mode[: -len("-partial")], True) if mode.endswith("-partial") else (mode, False)
+    eng = mk.Engine(shape, wdev, max_seq, mode=exec_mode, batch=B, attn_chunks=attn_chunks, partial_input=partial)
     k, v = device_cache(torch, shape, B, max_seq, wl.cache_filled)
     logits = torch.empty((B, shape.vocab), dtype=torch.float32, device="cuda")
     tok = torch.empty(B, dtype=torch.int32, device="cuda")
@@ -246,7 +247,8 @@ def main() -> int:
     ap.add_argument("--modes", default="mega,graph,multi,conv,conv-graph",
                     help="mega: the persistent megakernel; graph / multi: its executors one launch per stage, "
                          "captured or not; conv / conv-graph: the conventional one-kernel-per-operation path, "
-                         "eager or captured in a hipGraph")
+                         "eager or captured in a hipGraph; mega-partial: the megakernel with the partial-input "
+                         "down projection")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--attn-chunks", type=int, default=0, help="KV split per head (0: automatic)")
     ap.add_argument("--copy-mib", type=int, default=0,

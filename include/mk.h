@@ -75,7 +75,12 @@ extern "C" {
  * value is a budget of -watchdog_ms device clock ticks, which lets tests drive
  * the timeout path with every workgroup still leaving the kernel normally).
  * trace: non-zero records, for every (workgroup, stage) of the latest step,
- * four device wall-clock stamps (see mk_trace_copy); off for timing runs. */
+ * four device wall-clock stamps (see mk_trace_copy); off for timing runs.
+ * partial_input: non-zero starts every wave of the down projection as soon as
+ * its quarter of the gate/up output is ready instead of waiting for all of it
+ * (the pages' operations that begin on partial input; batch 1, head_dim 64;
+ * a separate kernel build, slower than the default on MI355X, see the
+ * repository's design notes). */
 typedef struct mk_config {
   int32_t n_layers;
   int32_t hidden;
@@ -94,7 +99,8 @@ typedef struct mk_config {
   int32_t num_wgs;
   int32_t watchdog_ms;
   int32_t trace;
-  int32_t reserved[6];
+  int32_t partial_input;
+  int32_t reserved[5];
 } mk_config;
 
 /* Device pointers to one layer's bf16 weights (row-major [out][in]):

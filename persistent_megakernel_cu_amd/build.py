@@ -24,13 +24,14 @@ LIB = os.path.join(PKG, "libmk.so")
 OBJ_DIR = os.path.join(ROOT, "_build")
 ARCH = os.environ.get("MK_OFFLOAD_ARCH", "gfx950")
 
-INSTANCES = [(g, d, b) for (g, d, b) in
-             [(1, 64, 0), (2, 64, 0), (4, 64, 0), (1, 128, 0), (2, 128, 0), (4, 128, 0),
-              (1, 64, 1), (2, 64, 1), (4, 64, 1)]]
+# (query heads per kv head, head_dim, batched, partial-input down projection)
+INSTANCES = [(1, 64, 0, 0), (2, 64, 0, 0), (4, 64, 0, 0), (1, 128, 0, 0), (2, 128, 0, 0), (4, 128, 0, 0),
+             (1, 64, 1, 0), (2, 64, 1, 0), (4, 64, 1, 0), (1, 64, 0, 1), (2, 64, 0, 1), (4, 64, 0, 1)]
 UNITS = ([("mk_kernels", "mk_kernels.hip", []), ("mk_api", "mk_api.cpp", []), ("mk_plan", "mk_plan.cpp", []),
           ("conv_kernels", "conv_kernels.hip", [])]
-         + [(f"mk_inst_{g}_{d}_{b}", "mk_inst.hip", [f"-DMK_INST_G={g}", f"-DMK_INST_D={d}", f"-DMK_INST_B={b}"])
-            for (g, d, b) in INSTANCES])
+         + [(f"mk_inst_{g}_{d}_{b}_{p}", "mk_inst.hip",
+             [f"-DMK_INST_G={g}", f"-DMK_INST_D={d}", f"-DMK_INST_B={b}", f"-DMK_INST_P={p}"])
+            for (g, d, b, p) in INSTANCES])
 
 
 def hipcc() -> str:

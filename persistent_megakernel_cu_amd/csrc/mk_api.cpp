@@ -12,10 +12,10 @@
 #include "mk_plan.h"
 
 namespace mk {
-hipError_t configure_kernels(int G, int D, bool batched, int lds_bytes);
+hipError_t configure_kernels(int G, int D, bool batched, bool partial, int lds_bytes);
 hipError_t launch_tile_rows(const uint16_t* src, size_t sstride, int nsrc, int kcols, uint16_t* dst, int kp, int row0,
                             int rstep);
-hipError_t persistent_occupancy(int G, int D, bool batched, int lds_bytes, int* blocks_per_cu);
+hipError_t persistent_occupancy(int G, int D, bool batched, bool partial, int lds_bytes, int* blocks_per_cu);
 hipError_t launch_persistent(const Params& P, int lds_bytes, hipStream_t stream);
 hipError_t launch_stage(const Params& P, int s, int lds_bytes, hipStream_t stream);
 hipError_t launch_set_args(StepArgs* a, int pos, uint32_t epoch, hipStream_t stream);
@@ -172,6 +172,7 @@ Params make_params(mk_handle* h) {
   P.res_floats = p.res_floats;
   P.watchdog_ticks = h->watchdog_ticks;
   P.trace = h->trace;
+  P.partial = p.partial ? 1 : 0;
   return P;
 }
 
@@ -383,9 +384,9 @@ int mk_load(const mk_config* cfg, const mk_weights* w, mk_handle** out) {
   if (p.D != 64 || p.H > 2048) { release(h); return MK_E_UNSUPPORTED; }
 
   // persistent residency: one workgroup per compute unit must fit
-  HIP_OR(mk::configure_kernels(p.G, p.D, p.batched, p.lds_bytes));
+  HIP_OR(mk::configure_kernels(p.G, p.D, p.batched, p.partial, p.lds_bytes));
   int per_cu = 0;
-  HIP_OR(mk::persistent_occupancy(p.G, p.D, p.batched, p.lds_bytes, &per_cu));
+  HIP_OR(mk::persistent_occupancy(p.G, p.D, p.batched, p.partial, p.lds_bytes, &per_cu));
   if (per_cu < 1) { release(h); return MK_E_DEVICE; }
 
   // packed weights

@@ -482,6 +482,47 @@ __device__ __forceinline__ bool stage_normed(const Params& P, Ctx& c, float* dst
   return c.flags[0] == 0;
 }
 
+// This wave's columns [col0, col0 + 512 ug) of a tagged input vector of n
+// elements (columns n and above read as 0) into act[]: lane l holds columns
+// col0 + 512 u + 8 l .. + 8 of unit u.  Every word is polled until it carries
+// this step's tag, up to four units (eight 16-byte loads per lane) in flight
+// at a time.  Wave-level, no barrier; false if the wait gave up.
+__device__ __forceinline__ bool wave_stage_cols(const Params& P, Ctx& c, const tword* src, int n, int col0, int ug,
+                                                int stage) {
+  for (int u0 = 0; u0 < ug; u0 += 4) {
+    tword4 w[8];
+    int col[8];
+    bool live[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      col[j] = col0 + (u0 + (j >> 1)) * kUnitElems + c.lane * 8 + (j & 1) * 4;
+      live[j] = u0 + (j >> 1) < ug && col[j] < n;
+      w[j] = live[j] ? ld_tag4(src + col[j]) : ready_word4(c.epoch);
+    }
+    bool stop = false;
+    uint64_t t0 = 0;
+    while (true) {
+      bool ready = true;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ready &= tag4_ready(w[j], c.epoch);
+      if (ready) break;
+      if (poll_stop(P, t0, stage, tag_of(w[0].x))) {
+        stop = true;
+        break;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (live[j] && !tag4_ready(w[j], c.epoch)) w[j] = ld_tag4(src + col[j]);
+    }
+    if (__any(stop)) return false;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (u0 + (j >> 1) < ug)
+        *reinterpret_cast<float4*>(c.act + col[j]) = live[j] ? tag_value4(w[j]) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  return true;
+}
+
 // ---------------------------------------------------------------------------
 // the per-wave weight stream (LDS ring, loader running ahead of the consumer)
 // ---------------------------------------------------------------------------
@@ -776,6 +817,65 @@ __device__ __forceinline__ void lm_finish(const Params& P, Ctx& c, const Task& t
       P.out_token[0] = idx;
     }
   }
+}
+
+// The down projection with partial-input start (region bit kRegionPartial):
+// pairs cut into 8 items, the items of wave w all covering the same quarter
+// of the row, so each wave stages and polls only that quarter of h and starts
+// as soon as it is ready (the glossary entry "Megakernel", section "Wie eine
+// ganze Rechenkette in ein Programm passt", and the article's paragraph on
+// operations that begin on partial input); the residual rows are checked
+// after the products, and the split-item sums are added in item order after
+// the task's barrier, so results do not depend on arrival order.
+__device__ __forceinline__ bool down_partial(const Params& P, Ctx& c, Stream& st, const Task& t, int s) {
+  const int l = t.layer;
+  const int nr = 2 * (int)(t.a1 - t.a0);
+  const tword* rs = P.x_attn + (size_t)l * P.H + 2 * (int)t.a0;
+  tword rw = c.tid < nr ? ld_tag(rs + c.tid) : ready_word(c.epoch);
+  // the previous task's LDS readers (activation, partials, residual) are done
+  __syncthreads();
+  const uint32_t ks = 1u << t.kslog, hks = ks >> 1;
+  const int upi = (int)(t.nu >> t.kslog);
+  const uint32_t n_items = (t.a1 - t.a0) << t.kslog;
+  const int col = (int)((uint32_t)c.wave & (hks - 1u)) * upi;  // the wave's first unit inside its row
+  bool ok = true;
+  if ((uint32_t)c.wave < n_items) {
+    ok = wave_stage_cols(P, c, P.h + (size_t)l * P.F, P.F, col * kUnitElems, upi, s);
+    if (c.tr != nullptr && c.lane == 0) c.tr[4 + kWaves + c.wave] = wall_clock64();
+    if (c.wave == 0) mark(c, 1);
+    if (ok) {
+      const float* xa = c.act + c.lane * 8;
+      for (uint32_t i = (uint32_t)c.wave; i < n_items; i += kWaves) {
+        const float a = wave_sum(dot_units(P, st, c, xa, col, upi));
+        if (c.lane == 0) c.part[i] = a;
+      }
+    }
+    mark_wave(c);
+  }
+  if (c.tid < nr) {
+    uint64_t t0 = 0;
+    while (!tag_ready(rw, c.epoch)) {
+      if (poll_stop(P, t0, s, tag_of(rw))) {
+        ok = false;
+        break;
+      }
+      rw = ld_tag(rs + c.tid);
+    }
+    c.res[c.tid] = tag_value(rw);
+  }
+  if (!ok) c.flags[0] = 1;
+  __syncthreads();
+  if (c.flags[0]) return false;
+  c.rs = 1.f;
+  LmBest best{-__builtin_inff(), -1};
+  for (uint32_t pl = (uint32_t)c.tid; pl < t.a1 - t.a0; pl += kThreads) {
+    float v0 = 0.f, v1 = 0.f;
+    for (uint32_t k = 0; k < hks; ++k) v0 += c.part[pl * ks + k];
+    for (uint32_t k = hks; k < ks; ++k) v1 += c.part[pl * ks + k];
+    gemv_epilogue<OP_DOWN>(P, c, t, t.a0 + pl, v0, v1, best, true, true);
+  }
+  mark(c, 2);
+  return true;
 }
 
 template <int OP>
@@ -1828,7 +1928,10 @@ __device__ __forceinline__ bool attn_task_b(const Params& P, Ctx& c, const Task&
 
 // G query heads per kv head and head_dim D are template parameters so that a
 // kernel instance carries exactly one attention variant (register budget).
-template <int G, int D, bool BATCHED>
+// PARTIAL instances also carry the partial-input down projection; the others
+// do not contain its code at all (the step time of this kernel moves by
+// tens of microseconds with the size of the code it carries).
+template <int G, int D, bool BATCHED, bool PARTIAL>
 __device__ __forceinline__ void run_stages(const Params& P, int s_begin, int s_end) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   Ctx c;
@@ -1899,7 +2002,12 @@ __device__ __forceinline__ void run_stages(const Params& P, int s_begin, int s_e
         case OP_QKV: ok = gemv_task<OP_QKV>(P, c, st, t, s); break;
         case OP_OPROJ: ok = gemv_task<OP_OPROJ>(P, c, st, t, s); break;
         case OP_GU: ok = gemv_task<OP_GU>(P, c, st, t, s); break;
-        case OP_DOWN: ok = gemv_task<OP_DOWN>(P, c, st, t, s); break;
+        case OP_DOWN:
+          if constexpr (PARTIAL)
+            ok = (t.region & kRegionPartial) ? down_partial(P, c, st, t, s) : gemv_task<OP_DOWN>(P, c, st, t, s);
+          else
+            ok = gemv_task<OP_DOWN>(P, c, st, t, s);
+          break;
         case OP_LM: ok = gemv_task<OP_LM>(P, c, st, t, s); break;
         case OP_ATTN:
           if constexpr (G == 1)
@@ -1916,14 +2024,14 @@ __device__ __forceinline__ void run_stages(const Params& P, int s_begin, int s_e
   wait_all_vmem();
 }
 
-template <int G, int D, bool BATCHED>
+template <int G, int D, bool BATCHED, bool PARTIAL>
 __global__ void __launch_bounds__(kThreads, 1) mk_persistent(Params P) {
-  run_stages<G, D, BATCHED>(P, 0, P.num_stages);
+  run_stages<G, D, BATCHED, PARTIAL>(P, 0, P.num_stages);
 }
 
-template <int G, int D, bool BATCHED>
+template <int G, int D, bool BATCHED, bool PARTIAL>
 __global__ void __launch_bounds__(kThreads, 1) mk_stage(Params P, int s) {
-  run_stages<G, D, BATCHED>(P, s, s + 1);
+  run_stages<G, D, BATCHED, PARTIAL>(P, s, s + 1);
 }
 
 // Host-side handles of one kernel instance.

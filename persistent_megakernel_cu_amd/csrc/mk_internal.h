@@ -85,6 +85,7 @@ inline constexpr int gemm_chunk_tiles(int ktiles, bool split) {
 constexpr uint8_t kRegionLm = 1;      // weights are the LM head, not the arena
 constexpr uint8_t kRegionSplit = 2;   // batched: the block's chunks are split over two workgroups
 constexpr uint8_t kRegionHalf1 = 4;   // batched: this task walks the second half of the chunks
+constexpr uint8_t kRegionPartial = 8; // batch 1 down projection: every wave stages only its items' columns of h
 
 struct Task {
   uint8_t op;
@@ -176,6 +177,7 @@ struct Params {
   int32_t pos;
   uint32_t epoch;
   const StepArgs* dargs; // non-null: read pos and epoch from here (graph mode)
+  int32_t partial;       // the plan has partial-input down-projection tasks (selects the kernel instance)
 };
 
 // Trace record of one (workgroup, stage): entered, inputs ready, compute done,

@@ -41,46 +41,53 @@ __global__ void mk_advance_args(StepArgs* a) {
 // Kernel instances, each defined in its own build of mk_inst.hip: batch 1
 // for (G, D), G in {1, 2, 4}, D in {64, 128}; batched plans (head_dim 64
 // only) for G in {1, 2, 4}.
-KernelPair instance_1_64_0();
-KernelPair instance_2_64_0();
-KernelPair instance_4_64_0();
-KernelPair instance_1_128_0();
-KernelPair instance_2_128_0();
-KernelPair instance_4_128_0();
-KernelPair instance_1_64_1();
-KernelPair instance_2_64_1();
-KernelPair instance_4_64_1();
+KernelPair instance_1_64_0_0();
+KernelPair instance_2_64_0_0();
+KernelPair instance_4_64_0_0();
+KernelPair instance_1_128_0_0();
+KernelPair instance_2_128_0_0();
+KernelPair instance_4_128_0_0();
+KernelPair instance_1_64_1_0();
+KernelPair instance_2_64_1_0();
+KernelPair instance_4_64_1_0();
+KernelPair instance_1_64_0_1();
+KernelPair instance_2_64_0_1();
+KernelPair instance_4_64_0_1();
 
 namespace {
 
-KernelPair kernels_for(int G, int D, bool batched) {
-  if (batched) return G == 1 ? instance_1_64_1() : G == 2 ? instance_2_64_1() : instance_4_64_1();
-  if (D == 64) return G == 1 ? instance_1_64_0() : G == 2 ? instance_2_64_0() : instance_4_64_0();
-  return G == 1 ? instance_1_128_0() : G == 2 ? instance_2_128_0() : instance_4_128_0();
+// partial: the plan has partial-input down-projection tasks (batch 1, head_dim 64)
+KernelPair kernels_for(int G, int D, bool batched, bool partial) {
+  if (batched) return G == 1 ? instance_1_64_1_0() : G == 2 ? instance_2_64_1_0() : instance_4_64_1_0();
+  if (partial) return G == 1 ? instance_1_64_0_1() : G == 2 ? instance_2_64_0_1() : instance_4_64_0_1();
+  if (D == 64) return G == 1 ? instance_1_64_0_0() : G == 2 ? instance_2_64_0_0() : instance_4_64_0_0();
+  return G == 1 ? instance_1_128_0_0() : G == 2 ? instance_2_128_0_0() : instance_4_128_0_0();
 }
 
 }  // namespace
 
-hipError_t configure_kernels(int G, int D, bool batched, int lds_bytes) {
-  const KernelPair k = kernels_for(G, D, batched);
+hipError_t configure_kernels(int G, int D, bool batched, bool partial, int lds_bytes) {
+  const KernelPair k = kernels_for(G, D, batched, partial);
   hipError_t e = hipFuncSetAttribute(k.persistent, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
   if (e != hipSuccess) return e;
   return hipFuncSetAttribute(k.stage, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
 }
 
-hipError_t persistent_occupancy(int G, int D, bool batched, int lds_bytes, int* blocks_per_cu) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, kernels_for(G, D, batched).persistent, kThreads,
-                                                      lds_bytes);
+hipError_t persistent_occupancy(int G, int D, bool batched, bool partial, int lds_bytes, int* blocks_per_cu) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, kernels_for(G, D, batched, partial).persistent,
+                                                      kThreads, lds_bytes);
 }
 
 hipError_t launch_persistent(const Params& P, int lds_bytes, hipStream_t stream) {
   void* args[] = {const_cast<Params*>(&P)};
-  return hipLaunchKernel(kernels_for(P.G, P.D, P.B > 1).persistent, dim3(P.num_wgs), dim3(kThreads), args, lds_bytes, stream);
+  return hipLaunchKernel(kernels_for(P.G, P.D, P.B > 1, P.partial != 0).persistent, dim3(P.num_wgs), dim3(kThreads),
+                         args, lds_bytes, stream);
 }
 
 hipError_t launch_stage(const Params& P, int s, int lds_bytes, hipStream_t stream) {
   void* args[] = {const_cast<Params*>(&P), &s};
-  return hipLaunchKernel(kernels_for(P.G, P.D, P.B > 1).stage, dim3(P.num_wgs), dim3(kThreads), args, lds_bytes, stream);
+  return hipLaunchKernel(kernels_for(P.G, P.D, P.B > 1, P.partial != 0).stage, dim3(P.num_wgs), dim3(kThreads), args,
+                         lds_bytes, stream);
 }
 
 hipError_t launch_tile_rows(const uint16_t* src, size_t sstride, int nsrc, int kcols, uint16_t* dst, int kp, int row0,

@@ -89,6 +89,9 @@ int plan_build(const mk_config& c, int W, Plan& p) {
   p.QDp = round_up(p.QD, kRowAlign);
   p.Fp = round_up(p.F, kRowAlign);
   p.batched = p.B > 1;
+  if (c.partial_input && (p.batched || p.D != 64))
+    return fail(p, MK_E_UNSUPPORTED, "partial-input starts need batch 1 and head_dim 64");
+  p.partial = c.partial_input != 0;
   if (p.batched && (p.Hp > kChunkCols || p.QDp > kChunkCols))
     return fail(p, MK_E_UNSUPPORTED, "batched decode needs hidden and n_heads * head_dim <= 2048");
 
@@ -159,6 +162,16 @@ int plan_build(const mk_config& c, int W, Plan& p) {
       t.wofs = wofs;
       t.ntasks = n;
       t.kslog = op == OP_LM ? 0u : split_log2((uint32_t)(a1 - a0), nu);
+      // Partial-input plans (cfg.partial_input): the down projection's input
+      // (ffn wide) is produced by the gate/up stage, whose straggler tail is
+      // the longest.  Cut every pair into 8 items of nu / 8 units: the items
+      // of wave w all cover the same quarter of the row's columns, so each
+      // wave stages only that quarter of h and starts as soon as it carries
+      // this step's tag, without waiting for the rest of h.
+      if (p.partial && op == OP_DOWN && (nu / 2) % 4 == 0 && (a1 - a0) * 8 <= (uint64_t)kMaxItems) {
+        t.kslog = 3;
+        t.region |= kRegionPartial;
+      }
       if (op == OP_OPROJ || op == OP_DOWN) max_res_rows = std::max(max_res_rows, (int)(2 * (a1 - a0)));
     }
   };
@@ -393,7 +406,11 @@ int plan_validate(const Plan& p, std::string* why) {
       if (t.ntasks != count) return bad("task count");
       if ((kind == OP_OPROJ || kind == OP_DOWN) && 2 * (t.a1 - t.a0) > (uint32_t)p.res_floats)
         return bad("residual rows exceed LDS");
-      if (t.region != (kind == OP_LM ? 1 : 0)) return bad("weight region");
+      if (t.region & kRegionPartial) {
+        if (kind != OP_DOWN || t.kslog != 3 || (t.nu / 2) % 4 != 0) return bad("partial-input task geometry");
+      } else if (t.region != (kind == OP_LM ? 1 : 0)) {
+        return bad("weight region");
+      }
       if (t.kslog > 0) {
         const uint32_t ks = 1u << t.kslog;
         if (kind == OP_LM) return bad("LM head is never split");

@@ -73,6 +73,7 @@ def main() -> int:
     ap.add_argument("--workload", default="llama1b")
     ap.add_argument("--pos", type=int, default=0, help="position of the traced step (default: the workload's first)")
     ap.add_argument("--steps", type=int, default=4, help="greedy steps before and including the traced one")
+    ap.add_argument("--save", default="", help="also write the raw stamps and clock rate to this .npz file")
     args = ap.parse_args()
 
     import torch
@@ -118,6 +119,8 @@ def main() -> int:
     if st.code != 0:
         raise SystemExit(f"device status {st.code}")
 
+    if args.save:
+        np.savez(args.save, stamps=stamps, khz=khz)
     t = stage_table(stamps, khz)
     print(f"workload {wl.name}, traced step at position {last}: {t['step_us']:.1f} us "
           f"(traced build), {t['layers']} layers\n")

@@ -322,3 +322,21 @@ def test_watchdog_timeout_path(tiny_w):
         gpu.close()
     # the device is unaffected: a handle with the normal budget decodes to parity
     run_teacher_forced(TINY, tiny_w, 48, make_prompt(TINY, 4), 0, 2, mode="mega", label="after-timeout")
+
+
+def test_tiny_partial_input_down():
+    # partial-input down projection (ffn 2048: rows of 4 units, 8 items per pair,
+    # each wave staging a quarter of h); 16-token prompt and 8 greedy steps
+    sh = TINY.with_(ffn=2048)
+    w = make_weights(sh, master=12, gain_jitter=0.1)
+    for mode in ("mega", "multi"):
+        run_teacher_forced(sh, w, 48, make_prompt(sh, 16, master=12), 0, 8, mode=mode, partial_input=True,
+                           label="tiny-partial")
+
+
+def test_llama1b_partial_input_bench_workload(llama1b):
+    # the benchmarked workload, whole, with the partial-input down projection
+    w, o = llama1b
+    reps = run_teacher_forced(LLAMA_1B, w, 256, make_prompt(LLAMA_1B, 128), 0, 128, mode="mega", oracle_obj=o,
+                              partial_input=True, label="llama1b-partial-full")
+    assert len(reps) == 256

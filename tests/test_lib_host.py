@@ -183,3 +183,17 @@ def test_conv_rejects_bad_configs():
     n = ctypes.c_size_t()
     assert mkb.lib().mk_conv_workspace_size(None, ctypes.byref(n)) == mkb.MK_E_INVAL
     assert mkb.lib().mk_conv_decode_step(None, None, None, None, None, None, None, None, 0, None) == mkb.MK_E_INVAL
+
+
+def test_partial_input_plans():
+    # partial-input down projection: batch 1 and head_dim 64 only; the plan validates
+    info = mkb.plan_describe(LLAMA_1B, 256, 256, partial_input=True)
+    assert info.num_stages == 5 * LLAMA_1B.n_layers + 1
+    mkb.plan_describe(TINY.with_(ffn=2048), 48, 256, partial_input=True)
+    for kw in (dict(batch=2), ):
+        with pytest.raises(mkb.MkError) as e:
+            mkb.plan_describe(TINY, 48, 256, partial_input=True, **kw)
+        assert e.value.code == mkb.MK_E_UNSUPPORTED
+    with pytest.raises(mkb.MkError) as e:
+        mkb.plan_describe(LLAMA_8B, 2112, 256, partial_input=True)
+    assert e.value.code == mkb.MK_E_UNSUPPORTED
