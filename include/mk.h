@@ -75,7 +75,9 @@ extern "C" {
  * value is a budget of -watchdog_ms device clock ticks, which lets tests drive
  * the timeout path with every workgroup still leaving the kernel normally).
  * trace: non-zero records, for every (workgroup, stage) of the latest step,
- * four device wall-clock stamps (see mk_trace_copy); off for timing runs.
+ * the device wall-clock stamps of mk_trace_copy, in a kernel build of its own
+ * (head_dim 64, without partial_input; otherwise mk_load returns
+ * MK_E_UNSUPPORTED); off for timing runs.
  * partial_input: non-zero starts every wave of the down projection as soon as
  * its quarter of the gate/up output is ready instead of waiting for all of it
  * (the pages' operations that begin on partial input; batch 1, head_dim 64;

@@ -24,14 +24,19 @@ LIB = os.path.join(PKG, "libmk.so")
 OBJ_DIR = os.path.join(ROOT, "_build")
 ARCH = os.environ.get("MK_OFFLOAD_ARCH", "gfx950")
 
-# (query heads per kv head, head_dim, batched, partial-input down projection)
-INSTANCES = [(1, 64, 0, 0), (2, 64, 0, 0), (4, 64, 0, 0), (1, 128, 0, 0), (2, 128, 0, 0), (4, 128, 0, 0),
-             (1, 64, 1, 0), (2, 64, 1, 0), (4, 64, 1, 0), (1, 64, 0, 1), (2, 64, 0, 1), (4, 64, 0, 1)]
+# Kernel instances (query heads per kv head G, head_dim, batched, query heads
+# per attention task GT (0: both variants, chosen at run time), flags: 1 trace
+# stamps, 2 partial-input down projection).  Each instance carries only the
+# code its plans run; the library picks one per plan (mk_kernels.hip).
+INSTANCES = ([(g, 64, 0, gt, f) for f in (0, 2) for g in (1, 2, 4) for gt in sorted({1, g})]
+             + [(g, 64, 0, 0, 1) for g in (1, 2, 4)]
+             + [(g, 128, 0, 0, 0) for g in (1, 2, 4)]
+             + [(g, 64, 1, 0, f) for f in (0, 1) for g in (1, 2, 4)])
 UNITS = ([("mk_kernels", "mk_kernels.hip", []), ("mk_api", "mk_api.cpp", []), ("mk_plan", "mk_plan.cpp", []),
           ("conv_kernels", "conv_kernels.hip", [])]
-         + [(f"mk_inst_{g}_{d}_{b}_{p}", "mk_inst.hip",
-             [f"-DMK_INST_G={g}", f"-DMK_INST_D={d}", f"-DMK_INST_B={b}", f"-DMK_INST_P={p}"])
-            for (g, d, b, p) in INSTANCES])
+         + [(f"mk_inst_{g}_{d}_{b}_{gt}_{f}", "mk_inst.hip",
+             [f"-DMK_INST_G={g}", f"-DMK_INST_D={d}", f"-DMK_INST_B={b}", f"-DMK_INST_GT={gt}", f"-DMK_INST_F={f}"])
+            for (g, d, b, gt, f) in INSTANCES])
 
 
 def hipcc() -> str:

@@ -12,10 +12,12 @@
 #include "mk_plan.h"
 
 namespace mk {
-hipError_t configure_kernels(int G, int D, bool batched, bool partial, int lds_bytes);
+hipError_t configure_kernels(int G, int D, bool batched, int gt, bool trace, bool partial, int lds_bytes);
+bool kernels_exist(int G, int D, bool batched, int gt, bool trace, bool partial);
 hipError_t launch_tile_rows(const uint16_t* src, size_t sstride, int nsrc, int kcols, uint16_t* dst, int kp, int row0,
                             int rstep);
-hipError_t persistent_occupancy(int G, int D, bool batched, bool partial, int lds_bytes, int* blocks_per_cu);
+hipError_t persistent_occupancy(int G, int D, bool batched, int gt, bool trace, bool partial, int lds_bytes,
+                                int* blocks_per_cu);
 hipError_t launch_persistent(const Params& P, int lds_bytes, hipStream_t stream);
 hipError_t launch_stage(const Params& P, int s, int lds_bytes, hipStream_t stream);
 hipError_t launch_set_args(StepArgs* a, int pos, uint32_t epoch, hipStream_t stream);
@@ -384,9 +386,14 @@ int mk_load(const mk_config* cfg, const mk_weights* w, mk_handle** out) {
   if (p.D != 64 || p.H > 2048) { release(h); return MK_E_UNSUPPORTED; }
 
   // persistent residency: one workgroup per compute unit must fit
-  HIP_OR(mk::configure_kernels(p.G, p.D, p.batched, p.partial, p.lds_bytes));
+  const int gt = p.G / p.attn_slices;
+  if (!mk::kernels_exist(p.G, p.D, p.batched, gt, cfg->trace != 0, p.partial)) {
+    release(h);
+    return MK_E_UNSUPPORTED;
+  }
+  HIP_OR(mk::configure_kernels(p.G, p.D, p.batched, gt, cfg->trace != 0, p.partial, p.lds_bytes));
   int per_cu = 0;
-  HIP_OR(mk::persistent_occupancy(p.G, p.D, p.batched, p.partial, p.lds_bytes, &per_cu));
+  HIP_OR(mk::persistent_occupancy(p.G, p.D, p.batched, gt, cfg->trace != 0, p.partial, p.lds_bytes, &per_cu));
   if (per_cu < 1) { release(h); return MK_E_DEVICE; }
 
   // packed weights

@@ -1926,13 +1926,21 @@ __device__ __forceinline__ bool attn_task_b(const Params& P, Ctx& c, const Task&
 // the stage loop shared by the persistent kernel and the per-stage kernels
 // ---------------------------------------------------------------------------
 
+// Kernel instance flags.
+constexpr int kFlagTrace = 1;    // records the per-(workgroup, stage) trace stamps
+constexpr int kFlagPartial = 2;  // carries the partial-input down projection
+
 // G query heads per kv head and head_dim D are template parameters so that a
-// kernel instance carries exactly one attention variant (register budget).
-// PARTIAL instances also carry the partial-input down projection; the others
-// do not contain its code at all (the step time of this kernel moves by
-// tens of microseconds with the size of the code it carries).
-template <int G, int D, bool BATCHED, bool PARTIAL>
+// kernel instance carries exactly one attention variant (register budget):
+// GT query heads per attention task (1 or G), or GT = 0 for an instance that
+// carries both and picks at run time.  FLAGS adds the trace stamps or the
+// partial-input down projection; instances without them do not contain that
+// code at all (the step time of this kernel moves by 5-20 us with the size of
+// the code it carries: instruction-cache misses).
+template <int G, int D, bool BATCHED, int GT, int FLAGS>
 __device__ __forceinline__ void run_stages(const Params& P, int s_begin, int s_end) {
+  constexpr bool PARTIAL = (FLAGS & kFlagPartial) != 0;
+  constexpr bool TRACE = (FLAGS & kFlagTrace) != 0;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   Ctx c;
   c.b = (int)blockIdx.x;
@@ -1983,8 +1991,9 @@ __device__ __forceinline__ void run_stages(const Params& P, int s_begin, int s_e
 
   for (int s = s_begin; s < s_end; ++s) {
     const Task t = task_at(st.tape, s - s_begin);
-    c.tr = (P.trace != nullptr && t.op != OP_NONE) ? P.trace + ((size_t)c.b * P.num_stages + s) * kTraceStamps
-                                                   : nullptr;
+    if constexpr (TRACE)
+      c.tr = (P.trace != nullptr && t.op != OP_NONE) ? P.trace + ((size_t)c.b * P.num_stages + s) * kTraceStamps
+                                                     : nullptr;
     mark(c, 0);
     bool ok = true;
     if constexpr (BATCHED) {
@@ -2010,8 +2019,10 @@ __device__ __forceinline__ void run_stages(const Params& P, int s_begin, int s_e
           break;
         case OP_LM: ok = gemv_task<OP_LM>(P, c, st, t, s); break;
         case OP_ATTN:
-          if constexpr (G == 1)
+          if constexpr (G == 1 || GT == 1)
             ok = attn_task<1, D>(P, c, t, s);
+          else if constexpr (GT == G)
+            ok = attn_task<G, D>(P, c, t, s);
           else
             ok = P.attn_gt == 1 ? attn_task<1, D>(P, c, t, s) : attn_task<G, D>(P, c, t, s);
           break;
@@ -2024,14 +2035,14 @@ __device__ __forceinline__ void run_stages(const Params& P, int s_begin, int s_e
   wait_all_vmem();
 }
 
-template <int G, int D, bool BATCHED, bool PARTIAL>
+template <int G, int D, bool BATCHED, int GT, int FLAGS>
 __global__ void __launch_bounds__(kThreads, 1) mk_persistent(Params P) {
-  run_stages<G, D, BATCHED, PARTIAL>(P, 0, P.num_stages);
+  run_stages<G, D, BATCHED, GT, FLAGS>(P, 0, P.num_stages);
 }
 
-template <int G, int D, bool BATCHED, bool PARTIAL>
+template <int G, int D, bool BATCHED, int GT, int FLAGS>
 __global__ void __launch_bounds__(kThreads, 1) mk_stage(Params P, int s) {
-  run_stages<G, D, BATCHED, PARTIAL>(P, s, s + 1);
+  run_stages<G, D, BATCHED, GT, FLAGS>(P, s, s + 1);
 }
 
 // Host-side handles of one kernel instance.

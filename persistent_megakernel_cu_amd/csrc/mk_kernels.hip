@@ -38,56 +38,96 @@ __global__ void mk_advance_args(StepArgs* a) {
 // host-side launchers
 // ---------------------------------------------------------------------------
 
-// Kernel instances, each defined in its own build of mk_inst.hip: batch 1
-// for (G, D), G in {1, 2, 4}, D in {64, 128}; batched plans (head_dim 64
-// only) for G in {1, 2, 4}.
-KernelPair instance_1_64_0_0();
-KernelPair instance_2_64_0_0();
-KernelPair instance_4_64_0_0();
-KernelPair instance_1_128_0_0();
-KernelPair instance_2_128_0_0();
-KernelPair instance_4_128_0_0();
-KernelPair instance_1_64_1_0();
-KernelPair instance_2_64_1_0();
-KernelPair instance_4_64_1_0();
-KernelPair instance_1_64_0_1();
-KernelPair instance_2_64_0_1();
-KernelPair instance_4_64_0_1();
+// Kernel instances, each defined in its own build of mk_inst.hip, named
+// instance_<G>_<D>_<batched>_<GT>_<flags> (see run_stages).  Batch 1, head_dim
+// 64: one attention variant per instance (GT = 1 or G), plain, with the
+// partial-input down projection, or traced (both attention variants);
+// head_dim 128: both variants; batched plans: plain or traced.
+KernelPair instance_1_64_0_1_0();
+KernelPair instance_2_64_0_1_0();
+KernelPair instance_2_64_0_2_0();
+KernelPair instance_4_64_0_1_0();
+KernelPair instance_4_64_0_4_0();
+KernelPair instance_1_64_0_1_2();
+KernelPair instance_2_64_0_1_2();
+KernelPair instance_2_64_0_2_2();
+KernelPair instance_4_64_0_1_2();
+KernelPair instance_4_64_0_4_2();
+KernelPair instance_1_64_0_0_1();
+KernelPair instance_2_64_0_0_1();
+KernelPair instance_4_64_0_0_1();
+KernelPair instance_1_128_0_0_0();
+KernelPair instance_2_128_0_0_0();
+KernelPair instance_4_128_0_0_0();
+KernelPair instance_1_64_1_0_0();
+KernelPair instance_2_64_1_0_0();
+KernelPair instance_4_64_1_0_0();
+KernelPair instance_1_64_1_0_1();
+KernelPair instance_2_64_1_0_1();
+KernelPair instance_4_64_1_0_1();
 
 namespace {
 
-// partial: the plan has partial-input down-projection tasks (batch 1, head_dim 64)
-KernelPair kernels_for(int G, int D, bool batched, bool partial) {
-  if (batched) return G == 1 ? instance_1_64_1_0() : G == 2 ? instance_2_64_1_0() : instance_4_64_1_0();
-  if (partial) return G == 1 ? instance_1_64_0_1() : G == 2 ? instance_2_64_0_1() : instance_4_64_0_1();
-  if (D == 64) return G == 1 ? instance_1_64_0_0() : G == 2 ? instance_2_64_0_0() : instance_4_64_0_0();
-  return G == 1 ? instance_1_128_0_0() : G == 2 ? instance_2_128_0_0() : instance_4_128_0_0();
+// The instance for a plan: G query heads per kv head, head_dim D, batched or
+// not, gt query heads per attention task, trace stamps, partial-input down
+// projection.  {nullptr, nullptr} when no instance is built for the mix.
+KernelPair kernels_for(int G, int D, bool batched, int gt, bool trace, bool partial) {
+  const KernelPair none{nullptr, nullptr};
+  if (batched) {
+    if (D != 64 || partial) return none;
+    if (trace) return G == 1 ? instance_1_64_1_0_1() : G == 2 ? instance_2_64_1_0_1() : instance_4_64_1_0_1();
+    return G == 1 ? instance_1_64_1_0_0() : G == 2 ? instance_2_64_1_0_0() : instance_4_64_1_0_0();
+  }
+  if (D == 128) {
+    if (trace || partial) return none;
+    return G == 1 ? instance_1_128_0_0_0() : G == 2 ? instance_2_128_0_0_0() : instance_4_128_0_0_0();
+  }
+  if (trace) {
+    if (partial) return none;
+    return G == 1 ? instance_1_64_0_0_1() : G == 2 ? instance_2_64_0_0_1() : instance_4_64_0_0_1();
+  }
+  const bool one = gt == 1;
+  if (partial) {
+    if (G == 1) return instance_1_64_0_1_2();
+    if (G == 2) return one ? instance_2_64_0_1_2() : instance_2_64_0_2_2();
+    return one ? instance_4_64_0_1_2() : instance_4_64_0_4_2();
+  }
+  if (G == 1) return instance_1_64_0_1_0();
+  if (G == 2) return one ? instance_2_64_0_1_0() : instance_2_64_0_2_0();
+  return one ? instance_4_64_0_1_0() : instance_4_64_0_4_0();
+}
+
+KernelPair kernels_of(const Params& P) {
+  return kernels_for(P.G, P.D, P.B > 1, P.attn_gt, P.trace != nullptr, P.partial != 0);
 }
 
 }  // namespace
 
-hipError_t configure_kernels(int G, int D, bool batched, bool partial, int lds_bytes) {
-  const KernelPair k = kernels_for(G, D, batched, partial);
+bool kernels_exist(int G, int D, bool batched, int gt, bool trace, bool partial) {
+  return kernels_for(G, D, batched, gt, trace, partial).persistent != nullptr;
+}
+
+hipError_t configure_kernels(int G, int D, bool batched, int gt, bool trace, bool partial, int lds_bytes) {
+  const KernelPair k = kernels_for(G, D, batched, gt, trace, partial);
   hipError_t e = hipFuncSetAttribute(k.persistent, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
   if (e != hipSuccess) return e;
   return hipFuncSetAttribute(k.stage, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
 }
 
-hipError_t persistent_occupancy(int G, int D, bool batched, bool partial, int lds_bytes, int* blocks_per_cu) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, kernels_for(G, D, batched, partial).persistent,
-                                                      kThreads, lds_bytes);
+hipError_t persistent_occupancy(int G, int D, bool batched, int gt, bool trace, bool partial, int lds_bytes,
+                                int* blocks_per_cu) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      blocks_per_cu, kernels_for(G, D, batched, gt, trace, partial).persistent, kThreads, lds_bytes);
 }
 
 hipError_t launch_persistent(const Params& P, int lds_bytes, hipStream_t stream) {
   void* args[] = {const_cast<Params*>(&P)};
-  return hipLaunchKernel(kernels_for(P.G, P.D, P.B > 1, P.partial != 0).persistent, dim3(P.num_wgs), dim3(kThreads),
-                         args, lds_bytes, stream);
+  return hipLaunchKernel(kernels_of(P).persistent, dim3(P.num_wgs), dim3(kThreads), args, lds_bytes, stream);
 }
 
 hipError_t launch_stage(const Params& P, int s, int lds_bytes, hipStream_t stream) {
   void* args[] = {const_cast<Params*>(&P), &s};
-  return hipLaunchKernel(kernels_for(P.G, P.D, P.B > 1, P.partial != 0).stage, dim3(P.num_wgs), dim3(kThreads), args,
-                         lds_bytes, stream);
+  return hipLaunchKernel(kernels_of(P).stage, dim3(P.num_wgs), dim3(kThreads), args, lds_bytes, stream);
 }
 
 hipError_t launch_tile_rows(const uint16_t* src, size_t sstride, int nsrc, int kcols, uint16_t* dst, int kp, int row0,
