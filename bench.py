@@ -128,6 +128,9 @@ def time_mode(mk, torch, wl, wdev, mode, warmup, steps, max_seq, attn_chunks=0):
     from synth_inputs import make_prompt, make_start_token
 
     shape, B = wl.shape, wl.batch
+    steps_launch = mode == "mega-steps"  # all timed steps in one persistent launch (mk_decode_steps)
+    if steps_launch:
+        mode = "mega"
     exec_mode, partial = (mode[: -len("-partial")], True) if mode.endswith("-partial") else (mode, False)
     eng = mk.Engine(shape, wdev, max_seq, mode=exec_mode, batch=B, attn_chunks=attn_chunks, partial_input=partial)
     k, v = device_cache(torch, shape, B, max_seq, wl.cache_filled)
@@ -159,6 +162,18 @@ def time_mode(mk, torch, wl, wdev, mode, warmup, steps, max_seq, attn_chunks=0):
             per_pos[pos] = e0.elapsed_time(e1) / steps
         toks = [int(x) for x in out.cpu().tolist()]
         ms = sum(per_pos.values()) / len(per_pos)
+    elif steps_launch:
+        start = wl.start_pos
+        out = torch.empty((max(steps, warmup), B), dtype=torch.int32, device="cuda")
+        if warmup > 0:
+            eng.decode_steps(tok, start, warmup, k, v, out[:warmup], None, stream)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        eng.decode_steps(first, start, steps, k, v, out[:steps], None, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        toks = out[:steps].cpu().tolist()
     else:
         start = wl.start_pos
         for i in range(warmup):

@@ -202,6 +202,29 @@ int mk_load(const mk_config* cfg, const mk_weights* w, mk_handle** out);
 int mk_decode_step(mk_handle* h, const int32_t* d_token, int32_t pos, const mk_kv* kv,
                    float* out_logits, int32_t* out_token, hipStream_t stream);
 
+/* mk_decode_steps -- n_steps greedy decode steps at positions pos ..
+ * pos + n_steps - 1 for every sequence, the argmax of each step feeding the
+ * embedding gather of the next on the device.  In MK_MODE_MEGA this is ONE
+ * persistent launch that walks the task tape n_steps times (the glossary
+ * entry "Megakernel", section "Wie eine ganze Rechenkette in ein Programm
+ * passt": the kernel is started once and then keeps running): the last
+ * workgroup of each step's argmax publishes the next tokens as tagged words
+ * that every workgroup polls before the next step's first stage.  In every
+ * other mode the steps are issued one by one (in the graph modes a step whose
+ * pointers differ from the captured ones recaptures the graph).
+ * d_token[batch] (device int32): the first step's input tokens.
+ * out_tokens[n_steps][batch] (device int32): the greedy token of every step.
+ * out_logits: [n_steps][batch][vocab] device fp32, or NULL when the logits
+ * are not wanted (they then go to a buffer of the handle).  kv as in
+ * mk_decode_step: slots pos .. pos + n_steps - 1 are written.  Asynchronous
+ * on stream; allocates nothing and never synchronises.
+ * Errors: MK_E_INVAL (null pointers, n_steps < 1, misalignment), MK_E_RANGE
+ * (pos < 0 or pos + n_steps > max_seq), MK_E_STATE, MK_E_HIP.  A device error
+ * (bad token, watchdog) is latched as in mk_decode_step; later steps of the
+ * same call then stop early. */
+int mk_decode_steps(mk_handle* h, const int32_t* d_token, int32_t pos, int32_t n_steps, const mk_kv* kv,
+                    float* out_logits, int32_t* out_tokens, hipStream_t stream);
+
 /* mk_reset -- wait for the handle's last stream, clear every flag, counter and
  * latched error and restart the step count.  Weights and the caller's cache
  * are untouched; a new sequence simply starts at pos = 0.  The plan built by

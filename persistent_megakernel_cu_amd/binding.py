@@ -98,6 +98,9 @@ def lib() -> ctypes.CDLL:
         L.mk_decode_step.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(MkKv),
                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         L.mk_decode_step.restype = ctypes.c_int
+        L.mk_decode_steps.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.POINTER(MkKv), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.mk_decode_steps.restype = ctypes.c_int
         L.mk_reset.argtypes = [ctypes.c_void_p]
         L.mk_reset.restype = ctypes.c_int
         L.mk_free.argtypes = [ctypes.c_void_p]
@@ -259,6 +262,20 @@ class Engine:
                                   out_token.data_ptr(), ctypes.c_void_p(stream))
         if rc != MK_OK:
             raise MkError(rc, "mk_decode_step")
+
+    def decode_steps(self, token, pos: int, n_steps: int, kcache, vcache, out_tokens, out_logits=None,
+                     stream=None) -> None:
+        """Enqueue n_steps greedy steps (mk_decode_steps): token [batch] feeds the first,
+        out_tokens [n_steps][batch] receives every step's token, out_logits
+        [n_steps][batch][vocab] every step's logits (or None)."""
+        stream = _stream_handle(stream)
+        self._kv.k = kcache.data_ptr()
+        self._kv.v = vcache.data_ptr()
+        rc = lib().mk_decode_steps(self._h, token.data_ptr(), int(pos), int(n_steps), ctypes.byref(self._kv),
+                                   out_logits.data_ptr() if out_logits is not None else None,
+                                   out_tokens.data_ptr(), ctypes.c_void_p(stream))
+        if rc != MK_OK:
+            raise MkError(rc, "mk_decode_steps")
 
     def trace(self):
         """Stamps of the latest step as (numpy uint64 [wg][stage][4], clock kHz)."""

@@ -20,6 +20,7 @@ hipError_t persistent_occupancy(int G, int D, bool batched, int gt, bool trace, 
                                 int* blocks_per_cu);
 hipError_t launch_persistent(const Params& P, int lds_bytes, hipStream_t stream);
 hipError_t launch_stage(const Params& P, int s, int lds_bytes, hipStream_t stream);
+hipError_t launch_steps(const Params& P, int n_steps, int lds_bytes, hipStream_t stream);
 hipError_t launch_set_args(StepArgs* a, int pos, uint32_t epoch, hipStream_t stream);
 hipError_t launch_advance_args(StepArgs* a, hipStream_t stream);
 hipError_t conv_launch_set_pos(int32_t* d_pos, int pos, hipStream_t s);
@@ -35,7 +36,8 @@ namespace {
 constexpr uint32_t kEpochLimit = 1u << 20;
 
 struct Workspace {
-  size_t x_attn, x_ffn, q, kvcur, o, h, kpart, attn_part, attn_ctr, amax, amax_ctr, tokerr, abort_flag, status, dargs;
+  size_t x_attn, x_ffn, q, kvcur, o, h, kpart, attn_part, attn_ctr, amax, amax_ctr, tokerr, abort_flag, status, dargs,
+      tok_tag;
   size_t bytes;
 };
 
@@ -64,6 +66,7 @@ Workspace layout_workspace(const Plan& p) {
   w.abort_flag = take(cur, 4);
   w.status = take(cur, sizeof(mk::DevStatus));
   w.dargs = take(cur, sizeof(mk::StepArgs));
+  w.tok_tag = take(cur, B * 8);
   w.bytes = cur;
   return w;
 }
@@ -105,6 +108,8 @@ struct mk_handle {
   char* conv_ws = nullptr;
   size_t conv_ws_bytes = 0;
   int32_t* conv_pos = nullptr;
+  // logits of multi-step calls made without an output buffer: [batch][vocab]
+  float* logits_scratch = nullptr;
 };
 
 namespace {
@@ -123,6 +128,7 @@ void release(mk_handle* h) {
   if (h->trace) (void)hipFree(h->trace);
   if (h->conv_ws) (void)hipFree(h->conv_ws);
   if (h->conv_pos) (void)hipFree(h->conv_pos);
+  if (h->logits_scratch) (void)hipFree(h->logits_scratch);
   if (h->status_host) (void)hipHostFree(h->status_host);
   delete h;
 }
@@ -279,6 +285,7 @@ int load_conv(const mk_config* cfg, const mk_weights* w, mk_handle** out) {
   HIP_OR(hipHostMalloc(reinterpret_cast<void**>(&h->status_host), sizeof(mk::DevStatus), hipHostMallocMapped));
   std::memset(h->status_host, 0, sizeof(mk::DevStatus));
   HIP_OR(hipStreamCreateWithFlags(&h->capture_stream, hipStreamNonBlocking));
+  HIP_OR(hipMalloc(&h->logits_scratch, (size_t)cfg->batch * cfg->vocab * 4));
   HIP_OR(hipDeviceSynchronize());
   *out = h;
   return MK_OK;
@@ -500,6 +507,7 @@ int mk_load(const mk_config* cfg, const mk_weights* w, mk_handle** out) {
   HIP_OR(hipHostGetDevicePointer(reinterpret_cast<void**>(&h->status_host_dev), h->status_host, 0));
 
   HIP_OR(hipStreamCreateWithFlags(&h->capture_stream, hipStreamNonBlocking));
+  HIP_OR(hipMalloc(&h->logits_scratch, (size_t)p.B * p.V * 4));
   if (cfg->trace) {
     const size_t tb = (size_t)p.W * p.stages * mk::kTraceStamps * sizeof(uint64_t);
     HIP_OR(hipMalloc(&h->trace, tb));
@@ -570,6 +578,52 @@ int mk_decode_step(mk_handle* h, const int32_t* d_token, int32_t pos, const mk_k
       return MK_E_INVAL;
   }
   if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return MK_E_HIP;
+  }
+  h->last_stream = stream;
+  h->used = true;
+  return MK_OK;
+}
+
+int mk_decode_steps(mk_handle* h, const int32_t* d_token, int32_t pos, int32_t n_steps, const mk_kv* kv,
+                    float* out_logits, int32_t* out_tokens, hipStream_t stream) {
+  if (!h || !d_token || !kv || !out_tokens || n_steps < 1) return MK_E_INVAL;
+  const int B = h->cfg.batch, V = h->cfg.vocab;
+  if (pos < 0 || (int64_t)pos + n_steps > (int64_t)h->cfg.max_seq) return MK_E_RANGE;
+  if (h->conv || h->cfg.exec_mode != MK_MODE_MEGA) {
+    // every other mode: one step at a time, the tokens chained on the device
+    for (int i = 0; i < n_steps; ++i) {
+      const int32_t* tin = i == 0 ? d_token : out_tokens + (size_t)(i - 1) * B;
+      float* lg = out_logits ? out_logits + (size_t)i * B * V : h->logits_scratch;
+      const int rc = mk_decode_step(h, tin, pos + i, kv, lg, out_tokens + (size_t)i * B, stream);
+      if (rc != MK_OK) return rc;
+    }
+    return MK_OK;
+  }
+  if (h->plan.L > 0 && (!kv->k || !kv->v)) return MK_E_INVAL;
+  if ((reinterpret_cast<uintptr_t>(kv->k) | reinterpret_cast<uintptr_t>(kv->v)) & 3u) return MK_E_INVAL;
+  if ((reinterpret_cast<uintptr_t>(out_logits) | reinterpret_cast<uintptr_t>(out_tokens) |
+       reinterpret_cast<uintptr_t>(d_token)) & 3u)
+    return MK_E_INVAL;
+  if (reinterpret_cast<volatile int32_t*>(&h->status_host->code)[0] != MK_OK) return MK_E_STATE;
+  if ((uint64_t)h->epoch + (uint64_t)n_steps + 1 >= kEpochLimit) {
+    if (clear_workspace(h, stream) != MK_OK) return MK_E_HIP;
+    h->epoch = 0;
+    h->shadow_pos = -1;
+  }
+  Params P = make_params(h);
+  P.token = d_token;
+  P.kcache = kv->k;
+  P.vcache = kv->v;
+  P.logits = out_logits ? out_logits : h->logits_scratch;
+  P.logits_step = out_logits ? (int64_t)B * V : 0;
+  P.out_token = out_tokens;
+  P.pos = pos;
+  P.epoch = h->epoch + 1;
+  P.tok_tag = reinterpret_cast<uint64_t*>(h->ws + h->wl.tok_tag);
+  h->epoch += (uint32_t)n_steps;
+  if (mk::launch_steps(P, n_steps, h->plan.lds_bytes, stream) != hipSuccess) {
     (void)hipGetLastError();
     return MK_E_HIP;
   }

@@ -126,6 +126,11 @@ __device__ __forceinline__ tword4 ready_word4(uint32_t epoch) {
 __device__ __forceinline__ float4 tag_value4(tword4 w) {
   return make_float4(tag_value(w.x), tag_value(w.y), tag_value(w.z), tag_value(w.w));
 }
+// Two bf16 of a KV-cache row, stored at agent scope: a multi-step launch
+// reads the slot on other compute units in the next step.
+__device__ __forceinline__ void st_kv(uint16_t* dst, uint32_t v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(dst), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ uint64_t ld_u64_agent(const uint64_t* p) {
   return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -230,6 +235,9 @@ struct Ctx {
   float* red;         // [kWaves] scratch
   uint64_t* red64;    // [kWaves]
   int* flags;         // [0] abort seen, [1] last-arriver, [2] token
+  int* tok;           // [B] this step's input tokens (LDS)
+  float* logits;      // this step's logits [B][V]
+  int32_t* out_tok;   // this step's greedy tokens [B]
   float* part;        // [kMaxItems] partial sums of split items
   uint64_t* tr;       // trace record of the current stage, or null
   float rs;           // RMSNorm scale of the staged activation (1 if none)
@@ -398,7 +406,7 @@ __device__ __forceinline__ bool stage_normed(const Params& P, Ctx& c, float* dst
   const uint16_t* emb = nullptr;
   if (src == nullptr) {
     if (c.tid == 0) {
-      int tok = P.token[0];
+      int tok = c.tok[0];
       if (tok < 0 || tok >= P.V) {
         latch_error(P, MK_E_TOKEN, stage, (uint32_t)tok);
         __hip_atomic_store(&P.tokerr[0], c.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -559,16 +567,23 @@ struct Stream {
   uint32_t ring;  // LDS byte address of this wave's ring
   uint32_t tape;  // LDS byte address of the task record of stage s_begin
   int issued, consumed, lslot, cslot;
-  int ls, s_begin, s_end;
+  int ls, s_begin, s_end, period;  // stages s_begin .. s_end - 1, the tape repeating every `period`
   uint32_t litem, lnitems, lkslog, lupi, lu, la0, lnu;
   uint32_t lc, lnc, lch;  // batched: chunk, chunks per row, tiles per chunk
   const char* lbase;
   bool ldone;
 };
 
+// Record of stage s of the stream's tape column (multi-step launches walk it repeatedly).
+__device__ __forceinline__ Task stream_task(const Stream& st, int s) {
+  int idx = s - st.s_begin;
+  if (idx >= st.period) idx %= st.period;
+  return task_at(st.tape, idx);
+}
+
 __device__ __forceinline__ void loader_seek(const Params& P, Stream& st, int s, int b, int wave) {
   for (; s < st.s_end; ++s) {
-    const Task t = task_at(st.tape, s - st.s_begin);
+    const Task t = stream_task(st, s);
     if (op_is_gemv(t.op)) {
       const uint32_t n_items = (t.a1 - t.a0) << t.kslog;
       if ((uint32_t)wave < n_items) {
@@ -695,7 +710,7 @@ __device__ __forceinline__ bool gemv_prologue(const Params& P, Ctx& c, const Tas
       if (rs) {
         rw = ld_tag(rs + c.tid);
       } else {  // layer 0: the residual is the embedding row itself
-        int tok = P.token[0];
+        int tok = c.tok[0];
         tok = (tok < 0 || tok >= P.V) ? 0 : tok;
         rw |= (uint32_t)P.embed[(size_t)tok * P.H + r0 + c.tid] << 16;
       }
@@ -751,7 +766,7 @@ __device__ __forceinline__ void gemv_epilogue(const Params& P, Ctx& c, const Tas
         const int hk = rr / P.D;
         if (w0) {
           uint16_t* dst = P.kcache + (((size_t)l * P.NKV + hk) * P.S + c.pos) * P.D + j;
-          *reinterpret_cast<uint32_t*>(dst) = (uint32_t)k0 | ((uint32_t)k1 << 16);
+          st_kv(dst, (uint32_t)k0 | ((uint32_t)k1 << 16));
           st_tag(P.kvcur + (size_t)l * 2 * P.KVD + rr, bf16_to_f32(k0), tag);
         }
         if (w1) st_tag(P.kvcur + (size_t)l * 2 * P.KVD + rr + 1, bf16_to_f32(k1), tag);
@@ -762,7 +777,7 @@ __device__ __forceinline__ void gemv_epilogue(const Params& P, Ctx& c, const Tas
       const uint16_t b0 = f32_to_bf16(v0), b1 = f32_to_bf16(v1);
       if (w0) {
         uint16_t* dst = P.vcache + (((size_t)l * P.NKV + hv) * P.S + c.pos) * P.D + j;
-        *reinterpret_cast<uint32_t*>(dst) = (uint32_t)b0 | ((uint32_t)b1 << 16);
+        st_kv(dst, (uint32_t)b0 | ((uint32_t)b1 << 16));
         st_tag(P.kvcur + ((size_t)l * 2 + 1) * P.KVD + rr, bf16_to_f32(b0), tag);
       }
       if (w1) st_tag(P.kvcur + ((size_t)l * 2 + 1) * P.KVD + rr + 1, bf16_to_f32(b1), tag);
@@ -778,8 +793,8 @@ __device__ __forceinline__ void gemv_epilogue(const Params& P, Ctx& c, const Tas
     if (w0) st_tag(P.h + (size_t)l * P.F + pair, sg * v1, tag);
   } else if (OP == OP_LM) {
     if (w0) {
-      P.logits[r] = v0;
-      P.logits[r + 1] = v1;
+      c.logits[r] = v0;
+      c.logits[r + 1] = v1;
     }
     if (v0 > best.v) { best.v = v0; best.i = r; }
     if (v1 > best.v) { best.v = v1; best.i = r + 1; }
@@ -789,6 +804,10 @@ __device__ __forceinline__ void gemv_epilogue(const Params& P, Ctx& c, const Tas
 // Argmax stage 2: every LM task publishes its key; the last to arrive picks the token.
 __device__ __forceinline__ void lm_finish(const Params& P, Ctx& c, const Task& t, const LmBest& best) {
   if (c.lane == 0) c.red64[c.wave] = amax_key(best.v, best.i);
+  // multi-step launches: every wave's stores of this step (the KV append
+  // among them, read by the next step's attention on other CUs) complete
+  // before this workgroup is counted and the next step's token is published
+  if (P.tok_tag != nullptr) wait_all_vmem();
   __syncthreads();
   if (c.tid == 0) {
     uint64_t k = 0;
@@ -814,7 +833,10 @@ __device__ __forceinline__ void lm_finish(const Params& P, Ctx& c, const Task& t
     if (c.lane == 0) {
       int idx = k ? (int)(~(uint32_t)k) : -1;
       if (ld_u32_agent(P.tokerr) == c.epoch) idx = -1;
-      P.out_token[0] = idx;
+      c.out_tok[0] = idx;
+      if (P.tok_tag != nullptr)  // the next step's input token
+        __hip_atomic_store(P.tok_tag, ((uint64_t)(c.epoch + 1u) << 32) | (uint32_t)idx, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -1217,7 +1239,7 @@ __device__ __forceinline__ size_t seq_off(const Params& P, int n, int l, int len
 // Order: chunk, then the wave's items, then tiles.
 __device__ __forceinline__ void loader_seek_b(const Params& P, Stream& st, int s, int wave) {
   for (; s < st.s_end; ++s) {
-    const Task t = task_at(st.tape, s - st.s_begin);
+    const Task t = stream_task(st, s);
     if (op_is_gemv(t.op)) {
       const uint32_t n_items = (t.a1 - t.a0) << t.kslog;
       if ((uint32_t)wave < n_items) {
@@ -1354,7 +1376,7 @@ __device__ __forceinline__ bool stage_batch(const Params& P, Ctx& c, float* dst,
 // Input token of sequence n (a bad id latches MK_E_TOKEN, marks the sequence
 // and reads row 0 instead).
 __device__ __forceinline__ int token_of(const Params& P, const Ctx& c, int n, int stage, bool report) {
-  int tok = P.token[n];
+  int tok = c.tok[n];
   if (tok < 0 || tok >= P.V) {
     if (report) {
       latch_error(P, MK_E_TOKEN, stage, (uint32_t)tok);
@@ -1459,7 +1481,7 @@ __device__ __forceinline__ void epi_pair_b(const Params& P, const Ctx& c, int l,
         const uint16_t k0 = f32_to_bf16(y0), k1 = f32_to_bf16(y1);
         const int hk = rr / P.D;
         uint16_t* dst = P.kcache + ((seq_off(P, n, l, P.NKV) + hk) * P.S + c.pos) * P.D + j;
-        *reinterpret_cast<uint32_t*>(dst) = (uint32_t)k0 | ((uint32_t)k1 << 16);
+        st_kv(dst, (uint32_t)k0 | ((uint32_t)k1 << 16));
         tword* kv = P.kvcur + seq_off(P, n, l, 2 * P.KVD) + rr;
         st_tag(kv, bf16_to_f32(k0), tag);
         st_tag(kv + 1, bf16_to_f32(k1), tag);
@@ -1469,7 +1491,7 @@ __device__ __forceinline__ void epi_pair_b(const Params& P, const Ctx& c, int l,
       const int hv = rr / P.D, j = rr % P.D;
       const uint16_t b0 = f32_to_bf16(v0), b1 = f32_to_bf16(v1);
       uint16_t* dst = P.vcache + ((seq_off(P, n, l, P.NKV) + hv) * P.S + c.pos) * P.D + j;
-      *reinterpret_cast<uint32_t*>(dst) = (uint32_t)b0 | ((uint32_t)b1 << 16);
+      st_kv(dst, (uint32_t)b0 | ((uint32_t)b1 << 16));
       tword* kv = P.kvcur + seq_off(P, n, l, 2 * P.KVD) + P.KVD + rr;
       st_tag(kv, bf16_to_f32(b0), tag);
       st_tag(kv + 1, bf16_to_f32(b1), tag);
@@ -1486,7 +1508,7 @@ __device__ __forceinline__ void epi_row_b(const Params& P, const Ctx& c, const T
                                           const float* rsb, LmBestB& best) {
   if (OP == OP_LM) {
     v *= rsb[n];
-    P.logits[(size_t)n * P.V + r] = v;
+    c.logits[(size_t)n * P.V + r] = v;
     if (v > best.v) {
       best.v = v;
       best.i = r;
@@ -1531,7 +1553,10 @@ __device__ __forceinline__ void lm_finish_b(const Params& P, Ctx& c, const Task&
     if (c.lane == 0) {
       int idx = k ? (int)(~(uint32_t)k) : -1;
       if (ld_u32_agent(P.tokerr + n) == c.epoch) idx = -1;
-      P.out_token[n] = idx;
+      c.out_tok[n] = idx;
+      if (P.tok_tag != nullptr)  // the next step's input token
+        __hip_atomic_store(P.tok_tag + n, ((uint64_t)(c.epoch + 1u) << 32) | (uint32_t)idx, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -1686,7 +1711,7 @@ __device__ __forceinline__ bool gemm_task(const Params& P, Ctx& c, Stream& st, c
         if (OP == OP_LM) {
           // reduced values back into the first part's tile for the argmax scan
           c.part[(size_t)(j * ks) * (kTileRows * 16) + q * 16 + n] = v * rsb[n];
-          P.logits[(size_t)n * P.V + ((int)t.a0 + j) * kTileRows + q] = v * rsb[n];
+          c.logits[(size_t)n * P.V + ((int)t.a0 + j) * kTileRows + q] = v * rsb[n];
         } else if (split) {
           // the second half hands its sums over; the first half adds them to its own
           tword* kp = P.kpart + seq_off(P, n, l, 2 * P.H) + (OP == OP_DOWN ? P.H : 0) + ((int)t.a0 + j) * kTileRows + q;
@@ -1937,8 +1962,15 @@ constexpr int kFlagPartial = 2;  // carries the partial-input down projection
 // partial-input down projection; instances without them do not contain that
 // code at all (the step time of this kernel moves by 5-20 us with the size of
 // the code it carries: instruction-cache misses).
-template <int G, int D, bool BATCHED, int GT, int FLAGS>
-__device__ __forceinline__ void run_stages(const Params& P, int s_begin, int s_end) {
+//
+// STEPS launches run n_steps greedy steps in one launch (the glossary entry
+// "Megakernel", section "Wie eine ganze Rechenkette in ein Programm passt":
+// the kernel is started once and stays running): the stage loop walks the
+// tape n_steps times, each step with the next epoch and position, and every
+// step after the first takes its input tokens from the tagged words the
+// previous step's argmax published (P.tok_tag).
+template <int G, int D, bool BATCHED, int GT, int FLAGS, bool STEPS>
+__device__ __forceinline__ void run_stages(const Params& P, int s_begin, int s_end, int n_steps) {
   constexpr bool PARTIAL = (FLAGS & kFlagPartial) != 0;
   constexpr bool TRACE = (FLAGS & kFlagTrace) != 0;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -1961,7 +1993,11 @@ __device__ __forceinline__ void run_stages(const Params& P, int s_begin, int s_e
   c.red64 = reinterpret_cast<uint64_t*>(smem + P.lds_misc + 64);
   c.flags = reinterpret_cast<int*>(smem + P.lds_misc + 128);
   c.part = reinterpret_cast<float*>(smem + P.lds_part);
+  c.tok = reinterpret_cast<int*>(smem + P.lds_misc + 160);
+  c.logits = P.logits;
+  c.out_tok = P.out_token;
   if (c.tid < 4) c.flags[c.tid] = 0;
+  if (c.tid < P.B) c.tok[c.tid] = P.token[c.tid];
   c.tr = nullptr;
   // this workgroup's column of the tape, stages [s_begin, s_end), into LDS
   {
@@ -1979,7 +2015,8 @@ __device__ __forceinline__ void run_stages(const Params& P, int s_begin, int s_e
   st.tape = lds_byte(smem) + (uint32_t)P.lds_tape;
   st.issued = st.consumed = st.lslot = st.cslot = 0;
   st.s_begin = s_begin;
-  st.s_end = s_end;
+  st.s_end = STEPS ? s_begin + n_steps * (s_end - s_begin) : s_end;
+  st.period = s_end - s_begin;
   st.ldone = false;
   if constexpr (BATCHED) {
     loader_seek_b(P, st, s_begin, c.wave);
@@ -1989,7 +2026,34 @@ __device__ __forceinline__ void run_stages(const Params& P, int s_begin, int s_e
     top_up(P, st, c.b, c.wave, c.lane, kRing);
   }
 
-  for (int s = s_begin; s < s_end; ++s) {
+  for (int gs = s_begin; gs < st.s_end; ++gs) {
+    int s = gs;
+    if constexpr (STEPS) {
+      s = s_begin + (gs - s_begin) % st.period;
+      if (s == s_begin && gs != s_begin) {
+        // the next step: epoch, position, outputs, and the tokens the last one picked
+        ++c.epoch;
+        ++c.pos;
+        c.logits += P.logits_step;
+        c.out_tok += P.B;
+        bool stop = false;
+        if (c.tid < P.B) {
+          uint64_t w = ld_u64_agent(P.tok_tag + c.tid);
+          uint64_t t0 = 0;
+          while ((uint32_t)(w >> 32) != c.epoch) {
+            if (poll_stop(P, t0, s, (uint32_t)(w >> 32))) {
+              stop = true;
+              break;
+            }
+            w = ld_u64_agent(P.tok_tag + c.tid);
+          }
+          c.tok[c.tid] = (int32_t)(uint32_t)w;
+        }
+        if (stop) c.flags[0] = 1;
+        __syncthreads();
+        if (c.flags[0]) break;
+      }
+    }
     const Task t = task_at(st.tape, s - s_begin);
     if constexpr (TRACE)
       c.tr = (P.trace != nullptr && t.op != OP_NONE) ? P.trace + ((size_t)c.b * P.num_stages + s) * kTraceStamps
@@ -2037,18 +2101,24 @@ __device__ __forceinline__ void run_stages(const Params& P, int s_begin, int s_e
 
 template <int G, int D, bool BATCHED, int GT, int FLAGS>
 __global__ void __launch_bounds__(kThreads, 1) mk_persistent(Params P) {
-  run_stages<G, D, BATCHED, GT, FLAGS>(P, 0, P.num_stages);
+  run_stages<G, D, BATCHED, GT, FLAGS, false>(P, 0, P.num_stages, 1);
 }
 
 template <int G, int D, bool BATCHED, int GT, int FLAGS>
 __global__ void __launch_bounds__(kThreads, 1) mk_stage(Params P, int s) {
-  run_stages<G, D, BATCHED, GT, FLAGS>(P, s, s + 1);
+  run_stages<G, D, BATCHED, GT, FLAGS, false>(P, s, s + 1, 1);
+}
+
+template <int G, int D, bool BATCHED, int GT, int FLAGS>
+__global__ void __launch_bounds__(kThreads, 1) mk_persistent_steps(Params P, int n_steps) {
+  run_stages<G, D, BATCHED, GT, FLAGS, true>(P, 0, P.num_stages, n_steps);
 }
 
 // Host-side handles of one kernel instance.
 struct KernelPair {
   const void* persistent;
   const void* stage;
+  const void* steps;
 };
 
 }  // namespace mk

@@ -18,10 +18,12 @@ namespace mk {
 
 template __global__ void mk_persistent<MK_INST_ARGS>(Params);
 template __global__ void mk_stage<MK_INST_ARGS>(Params, int);
+template __global__ void mk_persistent_steps<MK_INST_ARGS>(Params, int);
 
 KernelPair MK_INSTANCE_NAME(MK_INST_G, MK_INST_D, MK_INST_B, MK_INST_GT, MK_INST_F)() {
   return {reinterpret_cast<const void*>(&mk_persistent<MK_INST_ARGS>),
-          reinterpret_cast<const void*>(&mk_stage<MK_INST_ARGS>)};
+          reinterpret_cast<const void*>(&mk_stage<MK_INST_ARGS>),
+          reinterpret_cast<const void*>(&mk_persistent_steps<MK_INST_ARGS>)};
 }
 
 }  // namespace mk

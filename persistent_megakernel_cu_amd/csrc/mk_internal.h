@@ -178,6 +178,12 @@ struct Params {
   uint32_t epoch;
   const StepArgs* dargs; // non-null: read pos and epoch from here (graph mode)
   int32_t partial;       // the plan has partial-input down-projection tasks (selects the kernel instance)
+  // multi-step launches: step i's greedy tokens are published as 64-bit words
+  // (epoch of step i + 1 in the high half, the token in the low half) that
+  // step i + 1 polls before its first stage; the full epoch cannot match a
+  // word left by an earlier launch
+  uint64_t* tok_tag;     // [B], or null for single-step launches
+  int64_t logits_step;   // floats between the logits of consecutive steps (0: one buffer reused)
 };
 
 // Trace record of one (workgroup, stage): entered, inputs ready, compute done,

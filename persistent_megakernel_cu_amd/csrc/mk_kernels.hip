@@ -72,7 +72,7 @@ namespace {
 // not, gt query heads per attention task, trace stamps, partial-input down
 // projection.  {nullptr, nullptr} when no instance is built for the mix.
 KernelPair kernels_for(int G, int D, bool batched, int gt, bool trace, bool partial) {
-  const KernelPair none{nullptr, nullptr};
+  const KernelPair none{nullptr, nullptr, nullptr};
   if (batched) {
     if (D != 64 || partial) return none;
     if (trace) return G == 1 ? instance_1_64_1_0_1() : G == 2 ? instance_2_64_1_0_1() : instance_4_64_1_0_1();
@@ -110,8 +110,9 @@ bool kernels_exist(int G, int D, bool batched, int gt, bool trace, bool partial)
 hipError_t configure_kernels(int G, int D, bool batched, int gt, bool trace, bool partial, int lds_bytes) {
   const KernelPair k = kernels_for(G, D, batched, gt, trace, partial);
   hipError_t e = hipFuncSetAttribute(k.persistent, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
-  if (e != hipSuccess) return e;
-  return hipFuncSetAttribute(k.stage, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+  if (e == hipSuccess) e = hipFuncSetAttribute(k.stage, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+  if (e == hipSuccess) e = hipFuncSetAttribute(k.steps, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+  return e;
 }
 
 hipError_t persistent_occupancy(int G, int D, bool batched, int gt, bool trace, bool partial, int lds_bytes,
@@ -123,6 +124,11 @@ hipError_t persistent_occupancy(int G, int D, bool batched, int gt, bool trace, 
 hipError_t launch_persistent(const Params& P, int lds_bytes, hipStream_t stream) {
   void* args[] = {const_cast<Params*>(&P)};
   return hipLaunchKernel(kernels_of(P).persistent, dim3(P.num_wgs), dim3(kThreads), args, lds_bytes, stream);
+}
+
+hipError_t launch_steps(const Params& P, int n_steps, int lds_bytes, hipStream_t stream) {
+  void* args[] = {const_cast<Params*>(&P), &n_steps};
+  return hipLaunchKernel(kernels_of(P).steps, dim3(P.num_wgs), dim3(kThreads), args, lds_bytes, stream);
 }
 
 hipError_t launch_stage(const Params& P, int s, int lds_bytes, hipStream_t stream) {

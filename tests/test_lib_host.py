@@ -11,7 +11,8 @@ from synth_inputs import LLAMA_1B, LLAMA_8B, TINY
 
 def test_exports_every_declared_function():
     names = mkb.header_functions()
-    assert set(names) == {"mk_load", "mk_decode_step", "mk_reset", "mk_free", "mk_status", "mk_error_string",
+    assert set(names) == {"mk_load", "mk_decode_step", "mk_decode_steps", "mk_reset", "mk_free", "mk_status",
+                          "mk_error_string",
                           "mk_plan_describe", "mk_trace_copy", "mk_conv_workspace_size", "mk_conv_decode_step",
                           "mk_conv_decode_step_static"}
     L = mkb.lib()
