@@ -175,9 +175,10 @@ typedef struct mk_handle mk_handle;
  * once and reused for every forward pass).  All device work runs on the null
  * stream and is complete on return.
  * Errors: MK_E_INVAL (bad cfg/pointers), MK_E_UNSUPPORTED (includes, for
- * now, head_dim 128 and hidden > 2048: such shapes plan on the host but are
- * not run), MK_E_DEVICE, MK_E_NOMEM, MK_E_HIP.  On error *out is NULL and
- * nothing leaks. */
+ * now, head_dim 128, hidden > 2048 and packed weights of 4 GiB or more in the
+ * megakernel modes: such plans build on the host but are not run),
+ * MK_E_DEVICE, MK_E_NOMEM, MK_E_HIP.  On error *out is NULL and nothing
+ * leaks. */
 int mk_load(const mk_config* cfg, const mk_weights* w, mk_handle** out);
 
 /* mk_decode_step -- one decode step at position pos for every sequence.

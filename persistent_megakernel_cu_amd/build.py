@@ -7,6 +7,10 @@ compiled to an object in _build/ (in parallel; the kernel instances are the
 builds of csrc/mk_inst.hip with their template parameters as defines), then
 linked into libmk.so.  Packed-FP32 instruction selection is disabled for the
 device code.
+
+The same call builds libmkcheck.so (host code only, g++): the planner plus the
+address walk of csrc/mk_check.cpp, which the CPU tests use to replay a plan's
+tape through the kernels' own index helpers.
 """
 
 from __future__ import annotations
@@ -21,6 +25,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmk.so")
+CHECK_LIB = os.path.join(PKG, "libmkcheck.so")
 OBJ_DIR = os.path.join(ROOT, "_build")
 ARCH = os.environ.get("MK_OFFLOAD_ARCH", "gfx950")
 
@@ -73,8 +78,25 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
         r = subprocess.run(cmd, capture_output=True, text=True)
         return name, obj, cmd, r
 
+    def build_check():
+        tmp = CHECK_LIB + ".tmp"
+        cmd = ["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include",
+               "-I", os.path.join(ROOT, "include"), os.path.join(CSRC, "mk_check.cpp"),
+               os.path.join(CSRC, "mk_plan.cpp"), "-o", tmp]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode == 0:
+            os.replace(tmp, CHECK_LIB)
+        return cmd, r
+
     with ThreadPoolExecutor(max_workers=jobs()) as ex:
+        check = ex.submit(build_check)
         results = list(ex.map(compile_unit, UNITS))
+        ccmd, cres = check.result()
+    if verbose:
+        print(" ".join(ccmd), flush=True)
+    if cres.returncode != 0:
+        sys.stderr.write(cres.stdout + cres.stderr)
+        raise RuntimeError("g++ failed building libmkcheck.so")
     failed = False
     for name, obj, cmd, r in results:
         if verbose:

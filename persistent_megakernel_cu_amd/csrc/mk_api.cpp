@@ -29,47 +29,13 @@ hipError_t conv_launch_advance_pos(int32_t* d_pos, hipStream_t s);
 
 using mk::Params;
 using mk::Plan;
+using mk::Workspace;
+using mk::layout_workspace;
 
 namespace {
 
 // Step tags restart (with a workspace clear) before epoch * tasks-per-stage could wrap a u32.
 constexpr uint32_t kEpochLimit = 1u << 20;
-
-struct Workspace {
-  size_t x_attn, x_ffn, q, kvcur, o, h, kpart, attn_part, attn_ctr, amax, amax_ctr, tokerr, abort_flag, status, dargs,
-      tok_tag;
-  size_t bytes;
-};
-
-size_t take(size_t& cur, size_t bytes) {
-  size_t at = cur;
-  cur = (cur + bytes + 255) / 256 * 256;
-  return at;
-}
-
-Workspace layout_workspace(const Plan& p) {
-  Workspace w{};
-  size_t cur = 0;
-  const size_t L = std::max(p.L, 1), B = p.B;
-  w.x_attn = take(cur, B * L * p.H * 4);
-  w.x_ffn = take(cur, B * L * p.H * 4);
-  w.q = take(cur, B * L * p.QD * 4);
-  w.kvcur = take(cur, B * L * 2 * p.KVD * 4);
-  w.o = take(cur, B * L * p.QD * 4);
-  w.h = take(cur, B * L * p.F * 4);
-  w.kpart = take(cur, B * L * 2 * p.H * 4);
-  w.attn_part = take(cur, B * L * p.NKV * p.C * p.G * (p.D + 2) * 4);
-  w.attn_ctr = take(cur, B * L * p.NKV * p.G * 4);
-  w.amax = take(cur, B * p.W * 8);
-  w.amax_ctr = take(cur, B * 4);
-  w.tokerr = take(cur, B * 4);
-  w.abort_flag = take(cur, 4);
-  w.status = take(cur, sizeof(mk::DevStatus));
-  w.dargs = take(cur, sizeof(mk::StepArgs));
-  w.tok_tag = take(cur, B * 8);
-  w.bytes = cur;
-  return w;
-}
 
 }  // namespace
 
@@ -154,20 +120,20 @@ Params make_params(mk_handle* h) {
   P.rope = h->rope;
   char* ws = h->ws;
   const Workspace& w = h->wl;
-  P.x_attn = reinterpret_cast<uint32_t*>(ws + w.x_attn);
-  P.x_ffn = reinterpret_cast<uint32_t*>(ws + w.x_ffn);
-  P.q = reinterpret_cast<uint32_t*>(ws + w.q);
-  P.kvcur = reinterpret_cast<uint32_t*>(ws + w.kvcur);
-  P.o = reinterpret_cast<uint32_t*>(ws + w.o);
-  P.h = reinterpret_cast<uint32_t*>(ws + w.h);
-  P.kpart = reinterpret_cast<uint32_t*>(ws + w.kpart);
-  P.attn_part = reinterpret_cast<float*>(ws + w.attn_part);
-  P.attn_ctr = reinterpret_cast<uint32_t*>(ws + w.attn_ctr);
-  P.amax = reinterpret_cast<uint64_t*>(ws + w.amax);
-  P.amax_ctr = reinterpret_cast<uint32_t*>(ws + w.amax_ctr);
-  P.tokerr = reinterpret_cast<uint32_t*>(ws + w.tokerr);
-  P.abort_flag = reinterpret_cast<uint32_t*>(ws + w.abort_flag);
-  P.status = reinterpret_cast<mk::DevStatus*>(ws + w.status);
+  P.x_attn = reinterpret_cast<uint32_t*>(ws + w.x_attn.off);
+  P.x_ffn = reinterpret_cast<uint32_t*>(ws + w.x_ffn.off);
+  P.q = reinterpret_cast<uint32_t*>(ws + w.q.off);
+  P.kvcur = reinterpret_cast<uint32_t*>(ws + w.kvcur.off);
+  P.o = reinterpret_cast<uint32_t*>(ws + w.o.off);
+  P.h = reinterpret_cast<uint32_t*>(ws + w.h.off);
+  P.kpart = reinterpret_cast<uint32_t*>(ws + w.kpart.off);
+  P.attn_part = reinterpret_cast<float*>(ws + w.attn_part.off);
+  P.attn_ctr = reinterpret_cast<uint32_t*>(ws + w.attn_ctr.off);
+  P.amax = reinterpret_cast<uint64_t*>(ws + w.amax.off);
+  P.amax_ctr = reinterpret_cast<uint32_t*>(ws + w.amax_ctr.off);
+  P.tokerr = reinterpret_cast<uint32_t*>(ws + w.tokerr.off);
+  P.abort_flag = reinterpret_cast<uint32_t*>(ws + w.abort_flag.off);
+  P.status = reinterpret_cast<mk::DevStatus*>(ws + w.status.off);
   P.status_host = h->status_host_dev;
   P.lds_act = p.lds_act;
   P.lds_res = p.lds_res;
@@ -213,7 +179,7 @@ int capture_graph(mk_handle* h, const Params& base) {
   if (h->gexec) { (void)hipGraphExecDestroy(h->gexec); h->gexec = nullptr; }
   if (h->graph) { (void)hipGraphDestroy(h->graph); h->graph = nullptr; }
   Params P = base;
-  P.dargs = reinterpret_cast<mk::StepArgs*>(h->ws + h->wl.dargs);
+  P.dargs = reinterpret_cast<mk::StepArgs*>(h->ws + h->wl.dargs.off);
   hipStream_t cs = h->capture_stream;
   if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) return MK_E_HIP;
   bool ok = true;
@@ -386,11 +352,17 @@ int mk_load(const mk_config* cfg, const mk_weights* w, mk_handle** out) {
   std::string why;
   if (mk::plan_validate(h->plan, &why) != MK_OK) { release(h); return MK_E_INVAL; }
   const Plan& p = h->plan;
-  // Shapes with head_dim 128 or hidden > 2048 are refused: the first run of
-  // such a shape (32 layers, hidden 4096, head_dim 128) ended in a GPU memory
-  // fault whose cause is not found yet.  Their plans still build and validate
-  // on the host.
-  if (p.D != 64 || p.H > 2048) { release(h); return MK_E_UNSUPPORTED; }
+  // Plans outside the envelope that has run on the GPU are refused: the
+  // first run of a shape with head_dim 128, hidden 4096 and a 14 GB weight
+  // arena (32 layers) ended in a GPU memory fault whose cause is not found
+  // yet; the host-side address walk of that plan finds every index in
+  // bounds.  So head_dim 128, hidden > 2048 and packed weights of 4 GiB or
+  // more are refused until the cause is known.  Such plans still build and
+  // validate on the host.
+  if (p.D != 64 || p.H > 2048 || p.arena_bytes + p.lm_bytes >= (4ull << 30)) {
+    release(h);
+    return MK_E_UNSUPPORTED;
+  }
 
   // persistent residency: one workgroup per compute unit must fit
   const int gt = p.G / p.attn_slices;
@@ -567,7 +539,7 @@ int mk_decode_step(mk_handle* h, const int32_t* d_token, int32_t pos, const mk_k
         if (capture_graph(h, P) != MK_OK) return MK_E_HIP;
         std::memcpy(h->g_ptrs, ptrs, sizeof(ptrs));
       }
-      auto* dargs = reinterpret_cast<mk::StepArgs*>(h->ws + h->wl.dargs);
+      auto* dargs = reinterpret_cast<mk::StepArgs*>(h->ws + h->wl.dargs.off);
       if (h->shadow_pos != pos || h->shadow_epoch != epoch) e = mk::launch_set_args(dargs, pos, epoch, stream);
       if (e == hipSuccess) e = hipGraphLaunch(h->gexec, stream);
       h->shadow_pos = pos + 1;
@@ -621,7 +593,7 @@ int mk_decode_steps(mk_handle* h, const int32_t* d_token, int32_t pos, int32_t n
   P.out_token = out_tokens;
   P.pos = pos;
   P.epoch = h->epoch + 1;
-  P.tok_tag = reinterpret_cast<uint64_t*>(h->ws + h->wl.tok_tag);
+  P.tok_tag = reinterpret_cast<uint64_t*>(h->ws + h->wl.tok_tag.off);
   h->epoch += (uint32_t)n_steps;
   if (mk::launch_steps(P, n_steps, h->plan.lds_bytes, stream) != hipSuccess) {
     (void)hipGetLastError();

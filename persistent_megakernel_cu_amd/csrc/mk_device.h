@@ -34,6 +34,7 @@
 #include <stdint.h>
 
 #include "../../include/mk.h"
+#include "mk_addr.h"
 #include "mk_internal.h"
 
 namespace mk {
@@ -415,7 +416,7 @@ __device__ __forceinline__ bool stage_normed(const Params& P, Ctx& c, float* dst
       c.flags[2] = tok;
     }
     __syncthreads();
-    emb = P.embed + (size_t)c.flags[2] * P.H;
+    emb = P.embed + addr::embed_row(c.flags[2], P.H);
   }
   // groups of 4 elements (n is a multiple of 4): one 16-byte load each
   float ss = 0.f;
@@ -606,9 +607,9 @@ __device__ __forceinline__ void loader_seek(const Params& P, Stream& st, int s, 
 
 __device__ __forceinline__ void loader_issue(const Params& P, Stream& st, int b, int wave, int lane) {
   if (st.ldone) return;
-  const uint32_t pair = st.la0 + (st.litem >> st.lkslog);
-  const uint32_t unit = (st.litem & ((1u << st.lkslog) - 1u)) * st.lupi + st.lu;
-  const char* g = st.lbase + ((uint64_t)pair * st.lnu + unit) * kUnitBytes + (uint32_t)lane * 16u;
+  const uint32_t pair = addr::item_pair(st.la0, st.litem, st.lkslog);
+  const uint32_t unit = addr::item_unit(st.litem, st.lkslog, st.lupi, st.lu);
+  const char* g = st.lbase + addr::unit_byte(pair, st.lnu, unit, (uint32_t)lane);
   dma_unit(g, st.ring + (uint32_t)st.lslot * kUnitBytes);
   ++st.issued;
   st.lslot = (st.lslot + 1 == kRing) ? 0 : st.lslot + 1;
@@ -665,10 +666,10 @@ __device__ __forceinline__ float dot_units(const Params& P, Stream& st, Ctx& c, 
   for (; j + 4 <= n; j += 4) {
     uint4 v[4];
     take4(P, st, c.b, c.wave, c.lane, v);
-    const float* x = xa + (col + j) * kUnitElems;
+    const float* x = xa + addr::act_unit(col + j, 0);
     a += (dot8(v[0], x) + dot8(v[1], x + kUnitElems)) + (dot8(v[2], x + 2 * kUnitElems) + dot8(v[3], x + 3 * kUnitElems));
   }
-  for (; j < n; ++j) a += dot8(consume_unit(P, st, c.b, c.wave, c.lane), xa + (col + j) * kUnitElems);
+  for (; j < n; ++j) a += dot8(consume_unit(P, st, c.b, c.wave, c.lane), xa + addr::act_unit(col + j, 0));
   return a;
 }
 
@@ -678,7 +679,7 @@ __device__ __forceinline__ float dot_units(const Params& P, Stream& st, Ctx& c, 
 
 // Residual input of layer l >= 1 (x after the previous layer).
 __device__ __forceinline__ const tword* x_in(const Params& P, int l) {
-  return P.x_ffn + (size_t)(l - 1) * P.H;
+  return P.x_ffn + addr::layer_off(l - 1, P.H);
 }
 
 template <int OP>
@@ -686,25 +687,26 @@ __device__ __forceinline__ bool gemv_prologue(const Params& P, Ctx& c, const Tas
   const int l = t.layer;
   c.rs = 1.f;
   if (OP == OP_QKV || OP == OP_LM) {
-    const float* g = OP == OP_QKV ? P.g_attn + (size_t)l * P.Hp : P.g_final;
+    const float* g = OP == OP_QKV ? P.g_attn + addr::layer_off(l, P.Hp) : P.g_final;
     // this position's cos/sin do not depend on the wait: load them first
     float rv = 0.f;
-    if (OP == OP_QKV && c.tid < P.D) rv = P.rope[(size_t)c.pos * P.D + c.tid];
+    if (OP == OP_QKV && c.tid < P.D) rv = P.rope[addr::rope_row(c.pos, P.D) + c.tid];
     if (!stage_normed(P, c, c.act, l == 0 ? nullptr : x_in(P, l), g, P.H, P.Hp, s)) return false;
     if (OP == OP_QKV) {
       if (c.tid < P.D) c.rope[c.tid] = rv;
       __syncthreads();
     }
   } else if (OP == OP_GU) {
-    if (!stage_normed(P, c, c.act, P.x_attn + (size_t)l * P.H, P.g_ffn + (size_t)l * P.Hp, P.H, P.Hp, s)) return false;
+    if (!stage_normed(P, c, c.act, P.x_attn + addr::layer_off(l, P.H), P.g_ffn + addr::layer_off(l, P.Hp), P.H, P.Hp, s))
+      return false;
   } else {  // OPROJ, DOWN: plain activation + residual rows of this task
     const int n = OP == OP_OPROJ ? P.QD : P.F;
     const int np = OP == OP_OPROJ ? P.QDp : P.Fp;
-    const tword* src = OP == OP_OPROJ ? P.o + (size_t)l * P.QD : P.h + (size_t)l * P.F;
+    const tword* src = OP == OP_OPROJ ? P.o + addr::layer_off(l, P.QD) : P.h + addr::layer_off(l, P.F);
     const int r0 = 2 * (int)t.a0, nr = 2 * (int)(t.a1 - t.a0);
     // The residual rows were produced at least two stages earlier: read them
     // into registers before waiting for the activation (nr <= 512 rows).
-    const tword* rs = OP == OP_OPROJ ? (l == 0 ? nullptr : x_in(P, l) + r0) : P.x_attn + (size_t)l * P.H + r0;
+    const tword* rs = OP == OP_OPROJ ? (l == 0 ? nullptr : x_in(P, l) + r0) : P.x_attn + addr::layer_off(l, P.H) + r0;
     tword rw = ready_word(c.epoch);
     if (c.tid < nr) {
       if (rs) {
@@ -712,7 +714,7 @@ __device__ __forceinline__ bool gemv_prologue(const Params& P, Ctx& c, const Tas
       } else {  // layer 0: the residual is the embedding row itself
         int tok = c.tok[0];
         tok = (tok < 0 || tok >= P.V) ? 0 : tok;
-        rw |= (uint32_t)P.embed[(size_t)tok * P.H + r0 + c.tid] << 16;
+        rw |= (uint32_t)P.embed[addr::embed_row(tok, P.H) + r0 + c.tid] << 16;
       }
     }
     const Seg seg[1] = {{c.act, src, n, 1.f}};
@@ -759,38 +761,38 @@ __device__ __forceinline__ void gemv_epilogue(const Params& P, Ctx& c, const Tas
       const float y0 = v0 * cs - v1 * sn;
       const float y1 = v0 * sn + v1 * cs;
       if (r < P.QD) {
-        if (w0) st_tag(P.q + (size_t)l * P.QD + r, y0, tag);
-        if (w1) st_tag(P.q + (size_t)l * P.QD + r + 1, y1, tag);
+        if (w0) st_tag(P.q + addr::layer_off(l, P.QD) + r, y0, tag);
+        if (w1) st_tag(P.q + addr::layer_off(l, P.QD) + r + 1, y1, tag);
       } else {
         const uint16_t k0 = f32_to_bf16(y0), k1 = f32_to_bf16(y1);
         const int hk = rr / P.D;
         if (w0) {
-          uint16_t* dst = P.kcache + (((size_t)l * P.NKV + hk) * P.S + c.pos) * P.D + j;
+          uint16_t* dst = P.kcache + addr::kv_slot(l, P.NKV, hk, P.S, c.pos, P.D) + j;
           st_kv(dst, (uint32_t)k0 | ((uint32_t)k1 << 16));
-          st_tag(P.kvcur + (size_t)l * 2 * P.KVD + rr, bf16_to_f32(k0), tag);
+          st_tag(P.kvcur + addr::kvcur_off(l, P.KVD, 0) + rr, bf16_to_f32(k0), tag);
         }
-        if (w1) st_tag(P.kvcur + (size_t)l * 2 * P.KVD + rr + 1, bf16_to_f32(k1), tag);
+        if (w1) st_tag(P.kvcur + addr::kvcur_off(l, P.KVD, 0) + rr + 1, bf16_to_f32(k1), tag);
       }
     } else {  // v rows
       const int rr = r - P.QD - P.KVD;
       const int hv = rr / P.D, j = rr % P.D;
       const uint16_t b0 = f32_to_bf16(v0), b1 = f32_to_bf16(v1);
       if (w0) {
-        uint16_t* dst = P.vcache + (((size_t)l * P.NKV + hv) * P.S + c.pos) * P.D + j;
+        uint16_t* dst = P.vcache + addr::kv_slot(l, P.NKV, hv, P.S, c.pos, P.D) + j;
         st_kv(dst, (uint32_t)b0 | ((uint32_t)b1 << 16));
-        st_tag(P.kvcur + ((size_t)l * 2 + 1) * P.KVD + rr, bf16_to_f32(b0), tag);
+        st_tag(P.kvcur + addr::kvcur_off(l, P.KVD, 1) + rr, bf16_to_f32(b0), tag);
       }
-      if (w1) st_tag(P.kvcur + ((size_t)l * 2 + 1) * P.KVD + rr + 1, bf16_to_f32(b1), tag);
+      if (w1) st_tag(P.kvcur + addr::kvcur_off(l, P.KVD, 1) + rr + 1, bf16_to_f32(b1), tag);
     }
   } else if (OP == OP_OPROJ || OP == OP_DOWN) {
-    tword* dst = (OP == OP_OPROJ ? P.x_attn : P.x_ffn) + (size_t)l * P.H + r;
+    tword* dst = (OP == OP_OPROJ ? P.x_attn : P.x_ffn) + addr::layer_off(l, P.H) + r;
     const int k = r - 2 * (int)t.a0;
     if (w0) st_tag(dst, c.res[k] + v0, tag);
     if (w1) st_tag(dst + 1, c.res[k + 1] + v1, tag);
   } else if (OP == OP_GU) {
     // pair = (gate row f, up row f): h_f = silu(gate) * up
     const float sg = v0 / (1.0f + __expf(-v0));
-    if (w0) st_tag(P.h + (size_t)l * P.F + pair, sg * v1, tag);
+    if (w0) st_tag(P.h + addr::layer_off(l, P.F) + pair, sg * v1, tag);
   } else if (OP == OP_LM) {
     if (w0) {
       c.logits[r] = v0;
@@ -852,7 +854,7 @@ __device__ __forceinline__ void lm_finish(const Params& P, Ctx& c, const Task& t
 __device__ __forceinline__ bool down_partial(const Params& P, Ctx& c, Stream& st, const Task& t, int s) {
   const int l = t.layer;
   const int nr = 2 * (int)(t.a1 - t.a0);
-  const tword* rs = P.x_attn + (size_t)l * P.H + 2 * (int)t.a0;
+  const tword* rs = P.x_attn + addr::layer_off(l, P.H) + 2 * (int)t.a0;
   tword rw = c.tid < nr ? ld_tag(rs + c.tid) : ready_word(c.epoch);
   // the previous task's LDS readers (activation, partials, residual) are done
   __syncthreads();
@@ -862,7 +864,7 @@ __device__ __forceinline__ bool down_partial(const Params& P, Ctx& c, Stream& st
   const int col = (int)((uint32_t)c.wave & (hks - 1u)) * upi;  // the wave's first unit inside its row
   bool ok = true;
   if ((uint32_t)c.wave < n_items) {
-    ok = wave_stage_cols(P, c, P.h + (size_t)l * P.F, P.F, col * kUnitElems, upi, s);
+    ok = wave_stage_cols(P, c, P.h + addr::layer_off(l, P.F), P.F, col * kUnitElems, upi, s);
     if (c.tr != nullptr && c.lane == 0) c.tr[4 + kWaves + c.wave] = wall_clock64();
     if (c.wave == 0) mark(c, 1);
     if (ok) {
@@ -914,8 +916,8 @@ __device__ __forceinline__ bool gemv_task(const Params& P, Ctx& c, Stream& st, c
       float4 xr[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        xr[2 * j] = *reinterpret_cast<const float4*>(xa + j * kUnitElems);
-        xr[2 * j + 1] = *reinterpret_cast<const float4*>(xa + j * kUnitElems + 4);
+        xr[2 * j] = *reinterpret_cast<const float4*>(xa + addr::act_unit(j, 0));
+        xr[2 * j + 1] = *reinterpret_cast<const float4*>(xa + addr::act_unit(j, 0) + 4);
       }
       bool first = false;
       for (uint32_t pair = t.a0 + (uint32_t)c.wave; pair < t.a1; pair += kWaves) {
@@ -1066,7 +1068,7 @@ __device__ __forceinline__ bool attn_task(const Params& P, Ctx& c, const Task& t
   const int len0 = (n + C - 1) / C;
   const int t0 = min(n, ch * len0), t1 = min(n, t0 + len0);
 
-  const size_t head_off = ((size_t)l * P.NKV + g) * P.S * D;
+  const size_t head_off = addr::kv_head(l, P.NKV, g, P.S, D);
   const int ds = c.tid % NT;               // dim slice
   const int pg = c.tid / NT;               // position group
   // Branch-free prefetch: a position out of range, or pos itself, reads slot
@@ -1081,16 +1083,17 @@ __device__ __forceinline__ bool attn_task(const Params& P, Ctx& c, const Task& t
     vr[j] = *reinterpret_cast<const uint4*>(P.vcache + o);
   }
 
-  float* qs = c.act;                       // [GT][D], pre-scaled by 1/sqrt(D)
-  float* kcur = qs + GT * D;               // [D]
-  float* vcur = kcur + D;                  // [D]
-  float* wpart = vcur + D;                 // [kWaves][GT][D]
-  float* wm = wpart + kWaves * GT * D;     // [kWaves][GT] per-wave max
-  float* wl = wm + kWaves * GT;            // [kWaves][GT] per-wave sum
+  const addr::AttnLds al = addr::attn_lds(GT, D);
+  float* qs = c.act + al.qs;               // [GT][D], pre-scaled by 1/sqrt(D)
+  float* kcur = c.act + al.kcur;           // [D]
+  float* vcur = c.act + al.vcur;           // [D]
+  float* wpart = c.act + al.wpart;         // [kWaves][GT][D]
+  float* wm = c.act + al.wm;               // [kWaves][GT] per-wave max
+  float* wl = c.act + al.wl;               // [kWaves][GT] per-wave sum
   {
-    const Seg seg[3] = {{qs, P.q + (size_t)l * P.QD + (size_t)(g * GQ + hq0) * D, GT * D, P.qscale},
-                        {kcur, P.kvcur + (size_t)l * 2 * P.KVD + (size_t)g * D, D, 1.f},
-                        {vcur, P.kvcur + ((size_t)l * 2 + 1) * P.KVD + (size_t)g * D, D, 1.f}};
+    const Seg seg[3] = {{qs, P.q + addr::head_off(l, P.QD, g, GQ, hq0, D), GT * D, P.qscale},
+                        {kcur, P.kvcur + addr::kvcur_off(l, P.KVD, 0) + (size_t)g * D, D, 1.f},
+                        {vcur, P.kvcur + addr::kvcur_off(l, P.KVD, 1) + (size_t)g * D, D, 1.f}};
     if (!stage_tagged(P, c, seg, s)) return false;
   }
   mark(c, 1);
@@ -1190,7 +1193,7 @@ __device__ __forceinline__ bool attn_task(const Params& P, Ctx& c, const Task& t
       Ls = fmaf(e, wl[w * GT + h], Ls);
     }
   }
-  tword* o = P.o + (size_t)l * P.QD + (size_t)(g * GQ + hq0) * D;
+  tword* o = P.o + addr::head_off(l, P.QD, g, GQ, hq0, D);
   if (C == 1) {
     if (c.tid < GT * D) st_tag(o + c.tid, A / Ls, c.epoch);
     return true;
@@ -1199,7 +1202,7 @@ __device__ __forceinline__ bool attn_task(const Params& P, Ctx& c, const Task& t
   // record {m[GQ], l[GQ], acc[GQ][D]}; the last chunk of (kv head, slice) merges
   const int stride = GQ * (D + 2);
   const int hg = hq0 + h;                  // head inside the kv head's group
-  float* mine = P.attn_part + (((size_t)l * P.NKV + g) * C + ch) * stride;
+  float* mine = P.attn_part + addr::attn_rec(l, P.NKV, g, C, ch, stride);
   if (c.tid < GT * D) st_f32_agent(mine + 2 * GQ + hq0 * D + c.tid, A);
   if (c.tid < GT * D && d == 0) {
     st_f32_agent(mine + hg, M);
@@ -1208,7 +1211,7 @@ __device__ __forceinline__ bool attn_task(const Params& P, Ctx& c, const Task& t
   wait_all_vmem();
   __syncthreads();
   if (c.tid == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(P.attn_ctr + ((size_t)l * P.NKV + g) * GQ + slice, 1u,
+    const uint32_t old = __hip_atomic_fetch_add(P.attn_ctr + addr::attn_ctr(l, P.NKV, g, GQ, slice), 1u,
                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     c.flags[1] = old == c.epoch * (uint32_t)C - 1u;
   }
@@ -1216,7 +1219,7 @@ __device__ __forceinline__ bool attn_task(const Params& P, Ctx& c, const Task& t
   // the {m, l} table reuses wpart (free after the barrier above):
   // 2 * C * GT <= kWaves * GT * D because C <= 256 <= 4 * D
   if (c.flags[1])
-    merge_chunks<GT, D, 16>(c, P.attn_part + ((size_t)l * P.NKV + g) * C * stride, C, stride, GQ, hq0, wpart, o);
+    merge_chunks<GT, D, 16>(c, P.attn_part + addr::attn_rec(l, P.NKV, g, C, 0, stride), C, stride, GQ, hq0, wpart, o);
   return true;
 }
 
@@ -1577,7 +1580,7 @@ __device__ __forceinline__ bool gemm_task(const Params& P, Ctx& c, Stream& st, c
   // ---- prologue: first chunk of the activation, norms, residual rows, RoPE
   if (OP == OP_QKV || OP == OP_GU || OP == OP_LM) {
     float rv = 0.f;
-    if (OP == OP_QKV && c.tid < P.D) rv = P.rope[(size_t)c.pos * P.D + c.tid];
+    if (OP == OP_QKV && c.tid < P.D) rv = P.rope[addr::rope_row(c.pos, P.D) + c.tid];
     if (OP == OP_QKV && l == 0) {
       // embedding rows of the batch's tokens
       __syncthreads();
@@ -1620,7 +1623,7 @@ __device__ __forceinline__ bool gemm_task(const Params& P, Ctx& c, Stream& st, c
       }
       c.res[i] = v;
     }
-    const tword* src = OP == OP_OPROJ ? P.o + (size_t)l * P.QD : P.h + (size_t)l * P.F;
+    const tword* src = OP == OP_OPROJ ? P.o + addr::layer_off(l, P.QD) : P.h + addr::layer_off(l, P.F);
     const int kfull = OP == OP_OPROJ ? P.QD : P.F;
     const int col0 = cb * ch * kTileCols;
     const int kc0 = max(0, min(ch * kTileCols, kfull - col0));  // 0: the half lies in the zero padding
@@ -1639,7 +1642,7 @@ __device__ __forceinline__ bool gemm_task(const Params& P, Ctx& c, Stream& st, c
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int cc = cb; cc < ce; ++cc) {
     if (cc > cb) {  // next chunk of the activation (one item per wave: acc carries over)
-      const tword* src = OP == OP_OPROJ ? P.o + (size_t)l * P.QD : P.h + (size_t)l * P.F;
+      const tword* src = OP == OP_OPROJ ? P.o + addr::layer_off(l, P.QD) : P.h + addr::layer_off(l, P.F);
       const int kfull = OP == OP_OPROJ ? P.QD : P.F;
       const int kcc = max(0, min(ch * kTileCols, kfull - cc * ch * kTileCols));
       if (!stage_batch(P, c, c.act, stride, src, (size_t)P.L * kfull, cc * ch * kTileCols, kcc, ch * kTileCols, s))

@@ -292,6 +292,35 @@ int plan_build(const mk_config& c, int W, Plan& p) {
   return MK_OK;
 }
 
+Workspace layout_workspace(const Plan& p) {
+  Workspace w{};
+  size_t cur = 0;
+  auto take = [&](size_t bytes) {
+    const WsBuf b{cur, bytes};
+    cur = (cur + bytes + 255) / 256 * 256;
+    return b;
+  };
+  const size_t L = std::max(p.L, 1), B = p.B;
+  w.x_attn = take(B * L * p.H * 4);
+  w.x_ffn = take(B * L * p.H * 4);
+  w.q = take(B * L * p.QD * 4);
+  w.kvcur = take(B * L * 2 * p.KVD * 4);
+  w.o = take(B * L * p.QD * 4);
+  w.h = take(B * L * p.F * 4);
+  w.kpart = take(B * L * 2 * p.H * 4);
+  w.attn_part = take(B * L * p.NKV * p.C * p.G * (p.D + 2) * 4);
+  w.attn_ctr = take(B * L * p.NKV * p.G * 4);
+  w.amax = take(B * p.W * 8);
+  w.amax_ctr = take(B * 4);
+  w.tokerr = take(B * 4);
+  w.abort_flag = take(4);
+  w.status = take(sizeof(DevStatus));
+  w.dargs = take(sizeof(StepArgs));
+  w.tok_tag = take(B * 8);
+  w.bytes = cur;
+  return w;
+}
+
 int plan_validate(const Plan& p, std::string* why) {
   auto bad = [&](const std::string& m) {
     if (why) *why = m;

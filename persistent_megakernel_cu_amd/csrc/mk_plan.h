@@ -48,6 +48,18 @@ uint64_t qkv_rows(const Plan& p);
 // (with p.error set).  Does not touch any GPU.
 int plan_build(const mk_config& cfg, int W, Plan& p);
 
+// Device workspace of a megakernel handle (one allocation): byte offset and
+// byte size of each buffer (see Params for their layouts).
+struct WsBuf {
+  size_t off, bytes;
+};
+struct Workspace {
+  WsBuf x_attn, x_ffn, q, kvcur, o, h, kpart, attn_part, attn_ctr, amax, amax_ctr, tokerr, abort_flag, status, dargs,
+      tok_tag;
+  size_t bytes;  // the whole allocation
+};
+Workspace layout_workspace(const Plan& p);
+
 // Check the tape: stage order, exact coverage of every row pair and every
 // attention (kv head, chunk), byte bounds of every task, LDS limits.
 int plan_validate(const Plan& p, std::string* why);

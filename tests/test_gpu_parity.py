@@ -167,7 +167,8 @@ def test_error_paths(tiny_w):
 
 
 @pytest.mark.skip(reason="the first run of the Llama-8B shape (head_dim 128, hidden 4096) faulted the GPU; the "
-                         "cause is not found yet and mk_load refuses head_dim 128 / hidden > 2048 until it is")
+                         "cause is not found yet (the host-side address walk of its plan finds every index in "
+                         "bounds) and mk_load refuses head_dim 128 / hidden > 2048 until it is")
 def test_llama8b_seeded_cache():
     # Llama-8B shape (head_dim 128, untied LM head) over a seeded 2048-slot
     # cache: two teacher-forced steps at positions 2048 and 2049
@@ -213,6 +214,24 @@ def test_llama8b_shape_refused():
     w = {name: dummy for name, _, _ in weight_shapes(LLAMA_8B)}
     with pytest.raises(mkb.MkError) as e:
         mkb.Engine(LLAMA_8B, w, 2112)
+    assert e.value.code == mkb.MK_E_UNSUPPORTED
+
+
+def test_large_arena_refused():
+    # packed weights of 4 GiB or more are outside the envelope that has run
+    # on the GPU (36 layers at Llama-1B widths pack 4.4 GB): refused before
+    # any weight is read
+    import torch
+
+    from persistent_megakernel_cu_amd import binding as mkb
+    from synth_inputs import weight_shapes
+
+    sh = LLAMA_1B.with_(n_layers=36)
+    assert mkb.plan_describe(sh, 256).weight_bytes >= 4 << 30
+    dummy = torch.zeros(16, dtype=torch.int16, device="cuda")
+    w = {name: dummy for name, _, _ in weight_shapes(sh)}
+    with pytest.raises(mkb.MkError) as e:
+        mkb.Engine(sh, w, 256)
     assert e.value.code == mkb.MK_E_UNSUPPORTED
 
 
