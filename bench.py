@@ -239,6 +239,103 @@ def cpu_baseline(wl, weights, budget_s: float = 12.0):
     }
 
 
+W2A8_LAYER = (("qkv", 6144, 4096), ("o", 4096, 4096), ("gate_up", 28672, 4096), ("down", 4096, 14336))
+W2A8_LAYERS = 32
+
+
+def w2a8_bench(mk, torch, passes: int = 10, warmup: int = 2) -> dict:
+    """The W2A8 matrix-vector product over a model's worth of projections:
+    the Llama-8B shape's four projections (QKV, O, gate/up, down) of 32
+    layers, each layer's matrices in their own buffers (1.75 GB of packed
+    weights, beyond the 256 MB last-level cache, so every pass streams them
+    from HBM).  Packed words are drawn on the device with every two-bit field
+    in {0, 1, 2} (timing only; parity is tested elsewhere).  A pass runs the
+    128 one-launch products from float32 inputs (mk_w2a8_linear: codes formed
+    in the kernel); the GEMV-only pass runs the 128 GEMVs on codes quantised
+    once (mk_w2a8_gemv)."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    mats = []
+    for _ in range(W2A8_LAYERS):
+        for name, rows, cols in W2A8_LAYER:
+            w = torch.randint(0, 1 << 32, (rows, cols // 16), dtype=torch.int64, device="cuda", generator=gen)
+            w = w ^ (((w >> 1) & w & 0x55555555) << 1)  # a field holding 3 becomes 1
+            w = torch.where(w >= 1 << 31, w - (1 << 32), w)  # the same 32 bits as int32
+            mats.append((name, rows, cols, w.to(torch.int32).contiguous()))
+    xs = {c: torch.randn(c, device="cuda", generator=gen) for c in (4096, 14336)}
+    xq = {c: torch.empty(c, dtype=torch.int8, device="cuda") for c in xs}
+    sc = {c: torch.empty(1, dtype=torch.float32, device="cuda") for c in xs}
+    gam = torch.ones(max(r for _, r, _ in W2A8_LAYER), device="cuda")
+    y = torch.empty(max(r for _, r, _ in W2A8_LAYER), device="cuda")
+
+    def one_pass(quantize: bool):
+        for name, rows, cols, w in mats:
+            if quantize:
+                mk.w2a8_linear(w, gam, rows, cols, xs[cols], y)
+            else:
+                mk.w2a8_gemv(w, gam, rows, cols, xq[cols], sc[cols], y)
+
+    def timed(quantize: bool) -> float:
+        for _ in range(warmup):
+            one_pass(quantize)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(passes):
+            one_pass(quantize)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / passes  # us per pass
+
+    for c in xs:
+        mk.w2a8_quantize(xs[c], xq[c], sc[c])
+    gemv_us = timed(False)
+    pass_us = timed(True)
+    # the kernel's streaming rate, launch overhead amortised: one launch over
+    # the 32 layers' gate/up rows as one tall matrix (940 MB)
+    tall_rows = W2A8_LAYERS * 28672
+    tall = torch.randint(0, 1 << 32, (tall_rows, 4096 // 16), dtype=torch.int64, device="cuda", generator=gen)
+    tall = tall ^ (((tall >> 1) & tall & 0x55555555) << 1)
+    tall = torch.where(tall >= 1 << 31, tall - (1 << 32), tall).to(torch.int32).contiguous()
+    tgam = torch.ones(tall_rows, device="cuda")
+    ty = torch.empty(tall_rows, device="cuda")
+    for _ in range(warmup):
+        mk.w2a8_gemv(tall, tgam, tall_rows, 4096, xq[4096], sc[4096], ty)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(passes):
+        mk.w2a8_gemv(tall, tgam, tall_rows, 4096, xq[4096], sc[4096], ty)
+    e1.record()
+    torch.cuda.synchronize()
+    tall_us = e0.elapsed_time(e1) * 1e3 / passes
+    tall_bytes = tall_rows * 4096 // 4 + 4096 + 8 * tall_rows
+    tall_gbps = tall_bytes / (tall_us * 1e-6) / 1e9
+    del tall, tgam, ty
+    wbytes = sum(r * c // 4 for _, r, c, _ in mats)
+    io_bytes = sum(c + 8 * r for _, r, c, _ in mats)  # codes in, scale + output per row
+    achieved = (wbytes + io_bytes) / (gemv_us * 1e-6) / 1e9
+    bf16_bytes = sum(2 * r * c for _, r, c, _ in mats)
+    del mats
+    torch.cuda.empty_cache()
+    return {
+        "workload": "Llama-8B projections (QKV 6144x4096, O 4096x4096, gate/up 28672x4096, down 4096x14336) "
+                    f"x {W2A8_LAYERS} layers, batch 1, ternary weights in 2 bits, int8 activations",
+        "launches_per_pass": len(W2A8_LAYER) * W2A8_LAYERS,
+        "pass_us": round(pass_us, 1),
+        "gemv_only_pass_us": round(gemv_us, 1),
+        "weight_bytes_per_pass": wbytes,
+        "bf16_weight_bytes_equivalent": bf16_bytes,
+        "gemv_only_pass_GBps": round(achieved, 1),
+        "tall_matrix": {"rows": tall_rows, "cols": 4096, "us_per_launch": round(tall_us, 1),
+                        "bytes_per_launch": tall_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(tall_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(tall_gbps / HBM_PEAK_GBPS, 4),
+                     "note": "mk_w2a8_gemv over the tall matrix: algorithmic bytes (packed weights, codes, "
+                             "scales, outputs) per launch / average launch time (HIP events)"},
+    }
+
+
 def copy_probe(mib: int) -> int:
     """Plain copies of known size: their FETCH_SIZE / WRITE_SIZE per dispatch
     against mib MiB give the factor that turns those counters into bytes."""
@@ -265,6 +362,8 @@ def main() -> int:
                          "eager or captured in a hipGraph; mega-partial: the megakernel with the partial-input "
                          "down projection")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-w2a8", action="store_true", help="skip the W2A8 matrix-vector leg")
+    ap.add_argument("--w2a8-only", action="store_true", help="only run the W2A8 matrix-vector leg")
     ap.add_argument("--attn-chunks", type=int, default=0, help="KV split per head (0: automatic)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run 4 device-to-device copies of this many MiB (calibrates HBM byte counters)")
@@ -281,6 +380,9 @@ def main() -> int:
     import persistent_megakernel_cu_amd.binding as mk
     from synth_inputs import WORKLOADS, make_weights
 
+    if args.w2a8_only:
+        print(json.dumps({"w2a8": w2a8_bench(mk, torch)}), flush=True)
+        return 0
     wl = WORKLOADS[args.workload]
     shape = wl.shape
     if wl.steps <= 0:
@@ -360,6 +462,12 @@ def main() -> int:
         out["speedup_vs_graph"] = round(results["graph"] / results["mega"], 3)
     if "conv-graph" in results and "mega" in results:
         out["speedup_vs_conv_graph"] = round(results["conv-graph"] / results["mega"], 3)
+    if not args.no_w2a8:
+        del wdev
+        torch.cuda.empty_cache()
+        out["w2a8"] = w2a8_bench(mk, torch)
+        print(f"[bench] w2a8: {out['w2a8']['pass_us']} us per pass, GEMV-only {out['w2a8']['gemv_only_pass_us']} us",
+              file=sys.stderr, flush=True)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(wl, weights)
     print(json.dumps(out), flush=True)

@@ -331,6 +331,51 @@ int mk_conv_decode_step_static(const mk_config* cfg, const mk_weights* w, const 
                                const int32_t* d_pos, const mk_kv* kv, float* out_logits, int32_t* out_token,
                                hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * W2A8 matrix-vector product: ternary weights (-1, 0, 1) stored in two bits,
+ * int8 activations.  After the page "BitNet 1.58bit GPU Inference Kernel:
+ * Revolutionaere Effizienz fuer KI-Modelle mit W2A8-Quantisierung"
+ * (dasgeld.co, body: two-bit weights and eight-bit activations, sixteen
+ * two-bit values packed per 32-bit word for parallel decoding, 4-wide int8
+ * dot products).  The page prints no quantiser; the activations are coded as
+ * in BitNet b1.58:
+ *   s = 127 / max(max_k |x_k|, 1e-5),  q_k = clamp(round_half_even(x_k * s), -128, 127)
+ *   y_r = (float(sum_k Q_rk q_k) * gamma_r) / s        (float32, in this order)
+ * with Q the ternary codes and gamma_r the scale of row r (per-row absmean,
+ * or one value repeated for a per-tensor scale).
+ * ------------------------------------------------------------------------- */
+
+/* mk_w2a8_pack -- host: ternary codes [rows][cols] (int8, each -1, 0 or 1,
+ * row-major) into the packed matrix [rows][cols / 16] (uint32): word w of a
+ * row holds columns 16 w .. 16 w + 15, column 16 w + 4 k + m as code + 1 at
+ * bits 8 m + 2 k (k, m in 0..3).  Both buffers are host memory owned by the
+ * caller.  Errors: MK_E_INVAL (cols not a multiple of 64, negative sizes, null
+ * pointers, a code outside -1..1; packed is then partly written). */
+int mk_w2a8_pack(const int8_t* codes, int rows, int cols, uint32_t* packed);
+
+/* mk_w2a8_quantize -- device: the int8 codes d_xq[cols] and the scale
+ * *d_scale of the float32 vector d_x[cols], as above, enqueued on stream (one
+ * workgroup).  0 <= cols <= 16384, cols a multiple of 64.  Non-finite inputs
+ * give unspecified codes.  Errors: MK_E_INVAL, MK_E_HIP. */
+int mk_w2a8_quantize(const float* d_x, int cols, int8_t* d_xq, float* d_scale, hipStream_t stream);
+
+/* mk_w2a8_gemv -- device: d_y[rows] (float32) from the packed matrix
+ * d_packed (mk_w2a8_pack's layout, 16-byte aligned), the row scales
+ * d_gamma[rows], the activation codes d_xq[cols] (16-byte aligned) and their
+ * scale *d_scale, enqueued on stream.  The integer sums are exact, so the
+ * result is bit-for-bit the formula above.  0 <= cols <= 16384, cols a
+ * multiple of 64; rows == 0 is a no-op.  Errors: MK_E_INVAL, MK_E_HIP. */
+int mk_w2a8_gemv(const uint32_t* d_packed, const float* d_gamma, int rows, int cols, const int8_t* d_xq,
+                 const float* d_scale, float* d_y, hipStream_t stream);
+
+/* mk_w2a8_linear -- device: the whole product from a float32 input in one
+ * launch: every workgroup finds max |x| over d_x[cols] (16-byte aligned) and
+ * codes the columns it needs itself, so the codes, the scale and d_y[rows]
+ * are bit-for-bit those of mk_w2a8_quantize followed by mk_w2a8_gemv.  Same
+ * sizes and errors as mk_w2a8_gemv. */
+int mk_w2a8_linear(const uint32_t* d_packed, const float* d_gamma, int rows, int cols, const float* d_x, float* d_y,
+                   hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -124,6 +124,17 @@ def lib() -> ctypes.CDLL:
                                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(MkKv),
                                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         L.mk_conv_decode_step_static.restype = ctypes.c_int
+        L.mk_w2a8_pack.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        L.mk_w2a8_pack.restype = ctypes.c_int
+        L.mk_w2a8_quantize.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+        L.mk_w2a8_quantize.restype = ctypes.c_int
+        L.mk_w2a8_gemv.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.mk_w2a8_gemv.restype = ctypes.c_int
+        L.mk_w2a8_linear.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_void_p]
+        L.mk_w2a8_linear.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -131,7 +142,7 @@ def lib() -> ctypes.CDLL:
 def header_functions() -> list[str]:
     """Names of the functions include/mk.h declares."""
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_\s\*]*?\b(mk_[a-z_]+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_\s\*]*?\b(mk_[a-z0-9_]+)\s*\(", text, re.M)))
 
 
 def error_string(code: int) -> str:
@@ -224,6 +235,46 @@ def conv_decode_step_static(shape, weights: dict, max_seq: int, token, d_pos, kc
     del layers
     if rc != MK_OK:
         raise MkError(rc, "mk_conv_decode_step_static")
+
+
+def w2a8_pack(codes):
+    """Host packing of ternary codes (numpy int8 [rows][cols]) into the
+    [rows][cols / 16] uint32 layout of mk_w2a8_pack."""
+    import numpy as np
+
+    codes = np.ascontiguousarray(codes, dtype=np.int8)
+    rows, cols = codes.shape
+    out = np.zeros((rows, cols // 16), dtype=np.uint32)
+    rc = lib().mk_w2a8_pack(codes.ctypes.data, rows, cols, out.ctypes.data)
+    if rc != MK_OK:
+        raise MkError(rc, "mk_w2a8_pack")
+    return out
+
+
+def w2a8_quantize(x, xq, scale, stream=None) -> None:
+    """mk_w2a8_quantize on device tensors: x float32 [cols] -> xq int8 [cols], scale float32 [1]."""
+    rc = lib().mk_w2a8_quantize(ctypes.c_void_p(x.data_ptr()), x.numel(), ctypes.c_void_p(xq.data_ptr()),
+                                ctypes.c_void_p(scale.data_ptr()), ctypes.c_void_p(_stream_handle(stream)))
+    if rc != MK_OK:
+        raise MkError(rc, "mk_w2a8_quantize")
+
+
+def w2a8_gemv(packed, gamma, rows: int, cols: int, xq, scale, y, stream=None) -> None:
+    """mk_w2a8_gemv on device tensors (packed uint32/int32 [rows][cols/16])."""
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr() if t is not None else 0)
+    rc = lib().mk_w2a8_gemv(ptr(packed), ptr(gamma), rows, cols, ptr(xq), ptr(scale), ptr(y),
+                            ctypes.c_void_p(_stream_handle(stream)))
+    if rc != MK_OK:
+        raise MkError(rc, "mk_w2a8_gemv")
+
+
+def w2a8_linear(packed, gamma, rows: int, cols: int, x, y, stream=None) -> None:
+    """mk_w2a8_linear on device tensors: y = W2A8 product of the float32 input x, one launch."""
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr() if t is not None else 0)
+    rc = lib().mk_w2a8_linear(ptr(packed), ptr(gamma), rows, cols, ptr(x), ptr(y),
+                              ctypes.c_void_p(_stream_handle(stream)))
+    if rc != MK_OK:
+        raise MkError(rc, "mk_w2a8_linear")
 
 
 class Engine:

@@ -38,7 +38,7 @@ INSTANCES = ([(g, 64, 0, gt, f) for f in (0, 2) for g in (1, 2, 4) for gt in sor
              + [(g, 128, 0, 0, 0) for g in (1, 2, 4)]
              + [(g, 64, 1, 0, f) for f in (0, 1) for g in (1, 2, 4)])
 UNITS = ([("mk_kernels", "mk_kernels.hip", []), ("mk_api", "mk_api.cpp", []), ("mk_plan", "mk_plan.cpp", []),
-          ("conv_kernels", "conv_kernels.hip", [])]
+          ("conv_kernels", "conv_kernels.hip", []), ("w2a8", "w2a8.hip", [])]
          + [(f"mk_inst_{g}_{d}_{b}_{gt}_{f}", "mk_inst.hip",
              [f"-DMK_INST_G={g}", f"-DMK_INST_D={d}", f"-DMK_INST_B={b}", f"-DMK_INST_GT={gt}", f"-DMK_INST_F={f}"])
             for (g, d, b, gt, f) in INSTANCES])

@@ -24,6 +24,13 @@ Recipe (every stream is a NumPy PCG64 generator seeded from a SeedSequence):
 * KV cache of sequence b: ``SeedSequence([master, 20000 + b])``, N(0, 1),
   bf16; generated per (layer, kv head) block in that order.
 * start token of sequence b: ``SeedSequence([master, 30000 + b])``, uniform.
+* W2A8 matrix-vector cases (``make_w2a8_case``): ``SeedSequence([master,
+  40000, rows, cols])``; ternary codes drawn directly (a uniform float32
+  u per weight: -1 below 0.345, +1 from 0.655, else 0), so -1 / 0 / +1 with
+  probabilities 0.345 / 0.31 / 0.345 (the shares that absmean coding gives a
+  Gaussian matrix); row scales 0.02 * U(0.8, 1.2) (the mean |w| of a trained
+  projection's row); activations N(0, 1) with one element in 512 scaled by
+  U(10, 40) (the outlier channels of decoder activations).
 
 Matrices are row-major ``[out][in]`` arrays of uint16 bf16 bit patterns.
 """
@@ -213,3 +220,18 @@ WORKLOADS = {
     "llama1b-b8": Workload("llama1b-b8", LLAMA_1B, 8, 1088, 0, 1024, 64, 1024),
     "llama8b": Workload("llama8b", LLAMA_8B, 1, 2112, 0, 2048, 64, 2048),
 }
+
+
+def make_w2a8_case(rows: int, cols: int, master: int = 0) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """(codes int8 [rows][cols] in {-1, 0, 1}, row scales float32 [rows],
+    activations float32 [cols]) for a W2A8 matrix-vector product."""
+    g = _rng(master, 40000, rows, cols)
+    u = g.random((rows, cols), dtype=np.float32)
+    codes = (u >= np.float32(0.345)).astype(np.int8) + (u >= np.float32(0.655)).astype(np.int8) - np.int8(1)
+    gamma = (0.02 * g.uniform(0.8, 1.2, size=rows)).astype(np.float32)
+    x = g.standard_normal(cols, dtype=np.float32)
+    if cols:
+        n_out = max(1, cols // 512)
+        idx = g.choice(cols, size=n_out, replace=False)
+        x[idx] *= g.uniform(10.0, 40.0, size=n_out).astype(np.float32)
+    return codes.astype(np.int8), gamma, x

@@ -14,7 +14,7 @@ def test_exports_every_declared_function():
     assert set(names) == {"mk_load", "mk_decode_step", "mk_decode_steps", "mk_reset", "mk_free", "mk_status",
                           "mk_error_string",
                           "mk_plan_describe", "mk_trace_copy", "mk_conv_workspace_size", "mk_conv_decode_step",
-                          "mk_conv_decode_step_static"}
+                          "mk_conv_decode_step_static", "mk_w2a8_pack", "mk_w2a8_quantize", "mk_w2a8_gemv", "mk_w2a8_linear"}
     L = mkb.lib()
     for n in names:
         assert getattr(L, n) is not None
