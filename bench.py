@@ -202,6 +202,57 @@ def time_mode(mk, torch, wl, wdev, mode, warmup, steps, max_seq, attn_chunks=0):
     return ms, toks, per_pos
 
 
+def prefill_bench(mk, torch, wl, wdev, max_seq, chunk: int = 8, reps: int = 3) -> dict:
+    """The workload's prompt run two ways on one GPU: as prefill calls of
+    `chunk` tokens (mk_config.prefill: each call the batched MFMA executors
+    over `chunk` consecutive tokens, reading the weights once) and as one
+    batch-1 megakernel decode step per token.  Each way `reps` times, every
+    time into a fresh cache; wall time from HIP events on the stream."""
+    from synth_inputs import make_prompt
+
+    shape = wl.shape
+    T = wl.prompt_len - wl.prompt_len % chunk
+    prompt = [int(t) for t in make_prompt(shape, wl.prompt_len, master=0)][:T]
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(eng, B, calls):
+        k, v = device_cache(torch, shape, 1, max_seq, 0)
+        logits = torch.empty((B, shape.vocab), dtype=torch.float32, device="cuda")
+        out = torch.empty(B, dtype=torch.int32, device="cuda")
+        toks = [torch.tensor(c, dtype=torch.int32, device="cuda") for c, _ in calls]
+        for (c, pos), t in zip(calls, toks):  # warm-up pass
+            eng.decode_step(t, pos, k, v, logits, out, stream)
+        torch.cuda.synchronize()
+        total = 0.0
+        for _ in range(reps):
+            k.zero_()
+            v.zero_()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for (c, pos), t in zip(calls, toks):
+                eng.decode_step(t, pos, k, v, logits, out, stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            total += e0.elapsed_time(e1)
+        return total / reps * 1e3  # us
+
+    eng = mk.Engine(shape, wdev, max_seq, mode="mega", batch=chunk, prefill=True)
+    pf_us = timed(eng, chunk, [(prompt[i:i + chunk], i) for i in range(0, T, chunk)])
+    eng.close()
+    eng = mk.Engine(shape, wdev, max_seq, mode="mega", batch=1)
+    dec_us = timed(eng, 1, [([t], i) for i, t in enumerate(prompt)])
+    eng.close()
+    return {
+        "prompt_tokens": T,
+        "chunk": chunk,
+        "prefill_us": round(pf_us, 1),
+        "prefill_tokens_per_s": round(T / (pf_us * 1e-6), 1),
+        "decode_steps_us": round(dec_us, 1),
+        "speedup": round(dec_us / pf_us, 3),
+    }
+
+
 def cpu_baseline(wl, weights, budget_s: float = 12.0):
     """Time the oracle on a bounded sample of the same workload (sequence 0)."""
     import numpy as np
@@ -363,6 +414,7 @@ def main() -> int:
                          "down projection")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-w2a8", action="store_true", help="skip the W2A8 matrix-vector leg")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prompt-prefill leg")
     ap.add_argument("--w2a8-only", action="store_true", help="only run the W2A8 matrix-vector leg")
     ap.add_argument("--attn-chunks", type=int, default=0, help="KV split per head (0: automatic)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -462,6 +514,10 @@ def main() -> int:
         out["speedup_vs_graph"] = round(results["graph"] / results["mega"], 3)
     if "conv-graph" in results and "mega" in results:
         out["speedup_vs_conv_graph"] = round(results["conv-graph"] / results["mega"], 3)
+    if not args.no_prefill and wl.prompt_len >= 8 and B == 1:
+        out["prefill"] = prefill_bench(mk, torch, wl, wdev, max_seq)
+        print(f"[bench] prefill: {out['prefill']['prefill_us']} us for {out['prefill']['prompt_tokens']} tokens "
+              f"(decode steps: {out['prefill']['decode_steps_us']} us)", file=sys.stderr, flush=True)
     if not args.no_w2a8:
         del wdev
         torch.cuda.empty_cache()

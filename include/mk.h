@@ -82,7 +82,17 @@ extern "C" {
  * its quarter of the gate/up output is ready instead of waiting for all of it
  * (the pages' operations that begin on partial input; batch 1, head_dim 64;
  * a separate kernel build, slower than the default on MI355X, see the
- * repository's design notes). */
+ * repository's design notes).
+ * prefill: non-zero makes the batch the next `batch` tokens of ONE sequence
+ * (2..8 tokens, the batched MFMA executors): mk_decode_step then takes the
+ * tokens of positions pos .. pos + batch - 1 in d_token[batch], kv points at
+ * that one sequence's cache ([1][n_layers][n_kv_heads][max_seq][head_dim]),
+ * every token attends to the cache below pos plus the tokens of this call up
+ * to itself (causal), their K/V go to slots pos .. pos + batch - 1, and
+ * out_logits[batch][vocab] / out_token[batch] are each token's next-token
+ * logits and greedy token: a prompt is run `batch` tokens per launch, each
+ * launch reading the weights once (the prompt as MFMA GEMM tasks).  Not with
+ * mk_decode_steps or the MK_MODE_CONV modes. */
 typedef struct mk_config {
   int32_t n_layers;
   int32_t hidden;
@@ -102,7 +112,8 @@ typedef struct mk_config {
   int32_t watchdog_ms;
   int32_t trace;
   int32_t partial_input;
-  int32_t reserved[5];
+  int32_t prefill;
+  int32_t reserved[4];
 } mk_config;
 
 /* Device pointers to one layer's bf16 weights (row-major [out][in]):

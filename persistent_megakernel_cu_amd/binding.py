@@ -47,7 +47,7 @@ class MkConfig(ctypes.Structure):
         ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_double), ("tie_embeddings", ctypes.c_int32),
         ("exec_mode", ctypes.c_int32), ("attn_chunks", ctypes.c_int32), ("num_wgs", ctypes.c_int32),
         ("watchdog_ms", ctypes.c_int32), ("trace", ctypes.c_int32), ("partial_input", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 5),
+        ("prefill", ctypes.c_int32), ("reserved", ctypes.c_int32 * 4),
     ]
 
 
@@ -150,7 +150,8 @@ def error_string(code: int) -> str:
 
 
 def make_config(shape, max_seq: int, batch: int = 1, mode: str | int = "mega", attn_chunks: int = 0,
-                num_wgs: int = 0, watchdog_ms: int = 0, trace: bool = False, partial_input: bool = False) -> MkConfig:
+                num_wgs: int = 0, watchdog_ms: int = 0, trace: bool = False, partial_input: bool = False,
+                prefill: bool = False) -> MkConfig:
     c = MkConfig()
     c.n_layers, c.hidden, c.n_heads = shape.n_layers, shape.hidden, shape.n_heads
     c.n_kv_heads, c.head_dim, c.ffn, c.vocab = shape.n_kv_heads, shape.head_dim, shape.ffn, shape.vocab
@@ -161,6 +162,7 @@ def make_config(shape, max_seq: int, batch: int = 1, mode: str | int = "mega", a
     c.attn_chunks, c.num_wgs, c.watchdog_ms = attn_chunks, num_wgs, watchdog_ms
     c.trace = 1 if trace else 0
     c.partial_input = 1 if partial_input else 0
+    c.prefill = 1 if prefill else 0
     return c
 
 
@@ -290,11 +292,13 @@ class Engine:
 
     def __init__(self, shape, weights: dict, max_seq: int, mode: str = "mega", batch: int = 1,
                  attn_chunks: int = 0, num_wgs: int = 0, watchdog_ms: int = 0, trace: bool = False,
-                 partial_input: bool = False):
+                 partial_input: bool = False, prefill: bool = False):
         self.shape = shape
         self.max_seq = max_seq
         self.batch = batch
-        self.cfg = make_config(shape, max_seq, batch, mode, attn_chunks, num_wgs, watchdog_ms, trace, partial_input)
+        self.prefill = prefill
+        self.cfg = make_config(shape, max_seq, batch, mode, attn_chunks, num_wgs, watchdog_ms, trace, partial_input,
+                               prefill)
         w, layers = weights_struct(shape, weights)
         self._weights = dict(weights)
         h = ctypes.c_void_p()

@@ -147,6 +147,7 @@ Params make_params(mk_handle* h) {
   P.watchdog_ticks = h->watchdog_ticks;
   P.trace = h->trace;
   P.partial = p.partial ? 1 : 0;
+  P.prefill = p.prefill ? 1 : 0;
   return P;
 }
 
@@ -232,6 +233,7 @@ int capture_conv_graph(mk_handle* h, const int32_t* d_token, const mk_kv* kv, fl
 // mk_load for MK_MODE_CONV / MK_MODE_CONV_GRAPH: no plan and no repack; the
 // caller's weights are read in place by the per-operation kernels.
 int load_conv(const mk_config* cfg, const mk_weights* w, mk_handle** out) {
+  if (cfg->prefill) return MK_E_UNSUPPORTED;
   size_t bytes = 0;
   int rc = mk_conv_workspace_size(cfg, &bytes);
   if (rc != MK_OK) return rc;
@@ -509,7 +511,8 @@ int mk_decode_step(mk_handle* h, const int32_t* d_token, int32_t pos, const mk_k
        reinterpret_cast<uintptr_t>(d_token)) & 3u)
     return MK_E_INVAL;
   if (h->conv) return decode_conv(h, d_token, pos, kv, out_logits, out_token, stream);
-  if (pos < 0 || pos >= h->plan.S) return MK_E_RANGE;
+  // prefill: the call covers positions pos .. pos + B - 1
+  if (pos < 0 || (int64_t)pos + (h->plan.prefill ? h->plan.B : 1) > h->plan.S) return MK_E_RANGE;
   if (reinterpret_cast<volatile int32_t*>(&h->status_host->code)[0] != MK_OK) return MK_E_STATE;
   if (h->epoch + 1 >= kEpochLimit) {
     if (clear_workspace(h, stream) != MK_OK) return MK_E_HIP;
@@ -561,6 +564,7 @@ int mk_decode_step(mk_handle* h, const int32_t* d_token, int32_t pos, const mk_k
 int mk_decode_steps(mk_handle* h, const int32_t* d_token, int32_t pos, int32_t n_steps, const mk_kv* kv,
                     float* out_logits, int32_t* out_tokens, hipStream_t stream) {
   if (!h || !d_token || !kv || !out_tokens || n_steps < 1) return MK_E_INVAL;
+  if (!h->conv && h->plan.prefill) return MK_E_UNSUPPORTED;  // a prefill handle runs one call per chunk
   const int B = h->cfg.batch, V = h->cfg.vocab;
   if (pos < 0 || (int64_t)pos + n_steps > (int64_t)h->cfg.max_seq) return MK_E_RANGE;
   if (h->conv || h->cfg.exec_mode != MK_MODE_MEGA) {

@@ -1473,7 +1473,8 @@ __device__ __forceinline__ void epi_pair_b(const Params& P, const Ctx& c, int l,
     if (r < P.QD + P.KVD) {
       const int rr = r < P.QD ? r : r - P.QD;
       const int j = rr % P.D;
-      const float cs = c.rope[j], sn = c.rope[j + 1];
+      const float* rp = c.rope + (P.prefill ? n * P.D : 0);  // prefill: token n sits at position pos + n
+      const float cs = rp[j], sn = rp[j + 1];
       const float y0 = v0 * cs - v1 * sn;
       const float y1 = v0 * sn + v1 * cs;
       if (r < P.QD) {
@@ -1483,7 +1484,9 @@ __device__ __forceinline__ void epi_pair_b(const Params& P, const Ctx& c, int l,
       } else {
         const uint16_t k0 = f32_to_bf16(y0), k1 = f32_to_bf16(y1);
         const int hk = rr / P.D;
-        uint16_t* dst = P.kcache + ((seq_off(P, n, l, P.NKV) + hk) * P.S + c.pos) * P.D + j;
+        // prefill: one cache, token n's slot pos + n
+        uint16_t* dst = P.kcache + ((seq_off(P, P.prefill ? 0 : n, l, P.NKV) + hk) * P.S + c.pos + (P.prefill ? n : 0)) *
+                                       P.D + j;
         st_kv(dst, (uint32_t)k0 | ((uint32_t)k1 << 16));
         tword* kv = P.kvcur + seq_off(P, n, l, 2 * P.KVD) + rr;
         st_tag(kv, bf16_to_f32(k0), tag);
@@ -1493,7 +1496,8 @@ __device__ __forceinline__ void epi_pair_b(const Params& P, const Ctx& c, int l,
       const int rr = r - P.QD - P.KVD;
       const int hv = rr / P.D, j = rr % P.D;
       const uint16_t b0 = f32_to_bf16(v0), b1 = f32_to_bf16(v1);
-      uint16_t* dst = P.vcache + ((seq_off(P, n, l, P.NKV) + hv) * P.S + c.pos) * P.D + j;
+      uint16_t* dst = P.vcache + ((seq_off(P, P.prefill ? 0 : n, l, P.NKV) + hv) * P.S + c.pos + (P.prefill ? n : 0)) *
+                                     P.D + j;
       st_kv(dst, (uint32_t)b0 | ((uint32_t)b1 << 16));
       tword* kv = P.kvcur + seq_off(P, n, l, 2 * P.KVD) + P.KVD + rr;
       st_tag(kv, bf16_to_f32(b0), tag);
@@ -1579,8 +1583,10 @@ __device__ __forceinline__ bool gemm_task(const Params& P, Ctx& c, Stream& st, c
 
   // ---- prologue: first chunk of the activation, norms, residual rows, RoPE
   if (OP == OP_QKV || OP == OP_GU || OP == OP_LM) {
+    // cos/sin of this step's position, or (prefill) of each token's position
+    const int nrope = P.prefill ? P.B * P.D : P.D;
     float rv = 0.f;
-    if (OP == OP_QKV && c.tid < P.D) rv = P.rope[addr::rope_row(c.pos, P.D) + c.tid];
+    if (OP == OP_QKV && c.tid < nrope) rv = P.rope[addr::rope_row(c.pos + c.tid / P.D, P.D) + c.tid % P.D];
     if (OP == OP_QKV && l == 0) {
       // embedding rows of the batch's tokens
       __syncthreads();
@@ -1596,7 +1602,7 @@ __device__ __forceinline__ bool gemm_task(const Params& P, Ctx& c, Stream& st, c
       if (!stage_batch(P, c, c.act, stride, src, (size_t)P.L * P.H, 0, P.H, P.H, s)) return false;
     }
     const float* g = OP == OP_QKV ? P.g_attn + (size_t)l * P.Hp : OP == OP_GU ? P.g_ffn + (size_t)l * P.Hp : P.g_final;
-    if (OP == OP_QKV && c.tid < P.D) c.rope[c.tid] = rv;
+    if (OP == OP_QKV && c.tid < nrope) c.rope[c.tid] = rv;
     norm_batch(P, c, c.act, stride, g, rsb);
   } else {
     // residual rows [r0, r0 + nr) of every sequence, then the activation
@@ -1780,6 +1786,46 @@ __device__ __forceinline__ bool gemm_task(const Params& P, Ctx& c, Stream& st, c
 // Batched attention: task (sequence nu, kv head a0, chunk a1); the chunk is
 // walked in blocks of kMaxChunk positions with each wave's running maximum,
 // sum and P.V rescaled from block to block.  Layout per block as in attn_task.
+// Prefill attention input: q of token n (G heads, scaled), then the k and v
+// rows of kv head g of every token of the step, into qs[G * D], kcur[B][D],
+// vcur[B][D]; element groups of 4, polled until they carry this step's tag
+// (one round: G * D + 2 * B * D <= 1280 words).  Ends with a barrier; false
+// if the wait was aborted.
+template <int G, int D>
+__device__ __forceinline__ bool stage_prefill_qkv(const Params& P, Ctx& c, int l, int g, int n, float* qs, float* kcur,
+                                                  float* vcur, int stage) {
+  const int total = G * D + 2 * P.B * D;
+  const int i = 4 * c.tid;  // one group per thread
+  const bool on = i < total;
+  const tword* src = P.q + seq_off(P, n, l, P.QD) + (size_t)g * G * D + i;
+  float* dst = qs + i;
+  float scale = P.qscale;
+  if (i >= G * D) {
+    const int e = i - G * D, m = e / (2 * D), r = e - m * 2 * D;  // token m, k (r < D) or v
+    src = P.kvcur + seq_off(P, on ? m : 0, l, 2 * P.KVD) + (r < D ? 0 : P.KVD) + (size_t)g * D + (r % D);
+    dst = (r < D ? kcur : vcur) + m * D + (r % D);
+    scale = 1.f;
+  }
+  tword4 w = on ? ld_tag4(src) : ready_word4(c.epoch);
+  uint64_t t0 = 0;
+  bool stop = false;
+  while (!tag4_ready(w, c.epoch)) {
+    if (poll_stop(P, t0, stage, tag_of(w.x))) {
+      stop = true;
+      break;
+    }
+    w = ld_tag4(src);
+  }
+  __syncthreads();  // the previous task's LDS readers are done
+  if (on && !stop) {
+    const float4 v = tag_value4(w);
+    *reinterpret_cast<float4*>(dst) = make_float4(v.x * scale, v.y * scale, v.z * scale, v.w * scale);
+  }
+  if (stop) c.flags[0] = 1;
+  __syncthreads();
+  return c.flags[0] == 0;
+}
+
 template <int G, int D>
 __device__ __forceinline__ bool attn_task_b(const Params& P, Ctx& c, const Task& t, int s) {
   constexpr int NT = D / 8;
@@ -1787,11 +1833,14 @@ __device__ __forceinline__ bool attn_task_b(const Params& P, Ctx& c, const Task&
   constexpr int NPASS = kMaxChunk / PPP;
   const int l = t.layer, g = (int)t.a0, ch = (int)t.a1, n = (int)t.nu;
   const int C = P.attn_chunks;
-  const int npos = c.pos + 1;
+  // prefill: token n of one sequence, at position pos + n, sees the cache
+  // below pos and this step's tokens 0..n (their k and v staged from kvcur)
+  const bool pf = P.prefill != 0;
+  const int npos = c.pos + (pf ? n : 0) + 1;
   const int len0 = (npos + C - 1) / C;
   const int t0 = min(npos, ch * len0), t1 = min(npos, t0 + len0);
 
-  const size_t head_off = (seq_off(P, n, l, P.NKV) + g) * P.S * D;
+  const size_t head_off = (seq_off(P, pf ? 0 : n, l, P.NKV) + g) * P.S * D;
   const int ds = c.tid % NT;
   const int pg = c.tid / NT;
   uint4 kr[NPASS], vr[NPASS];
@@ -1799,7 +1848,8 @@ __device__ __forceinline__ bool attn_task_b(const Params& P, Ctx& c, const Task&
 #pragma unroll
     for (int j = 0; j < NPASS; ++j) {
       const int tp = base + j * PPP + pg;
-      const int tl = (tp < t1 && tp != c.pos) ? tp : 0;
+      // slots from pos on are this step's (staged below); slot 0 stands in
+      const int tl = (tp < t1 && tp < c.pos) ? tp : 0;
       const size_t o = head_off + (size_t)tl * D + ds * 8;
       kr[j] = *reinterpret_cast<const uint4*>(P.kcache + o);
       vr[j] = *reinterpret_cast<const uint4*>(P.vcache + o);
@@ -1807,17 +1857,20 @@ __device__ __forceinline__ bool attn_task_b(const Params& P, Ctx& c, const Task&
   };
   prefetch(t0);
 
+  const int nrows = pf ? P.B : 1;  // k / v rows of this step in LDS
   float* qs = c.act;
   float* kcur = qs + G * D;
-  float* vcur = kcur + D;
-  float* wpart = vcur + D;
+  float* vcur = kcur + nrows * D;
+  float* wpart = vcur + nrows * D;
   float* wm = wpart + kWaves * G * D;
   float* wl = wm + kWaves * G;
-  {
+  if (!pf) {
     const Seg seg[3] = {{qs, P.q + seq_off(P, n, l, P.QD) + (size_t)g * G * D, G * D, P.qscale},
                         {kcur, P.kvcur + seq_off(P, n, l, 2 * P.KVD) + (size_t)g * D, D, 1.f},
                         {vcur, P.kvcur + seq_off(P, n, l, 2 * P.KVD) + P.KVD + (size_t)g * D, D, 1.f}};
     if (!stage_tagged(P, c, seg, s)) return false;
+  } else if (!stage_prefill_qkv<G, D>(P, c, l, g, n, qs, kcur, vcur, s)) {
+    return false;
   }
   mark(c, 1);
   float acc[G][8], ls[G], m[G];
@@ -1830,19 +1883,27 @@ __device__ __forceinline__ bool attn_task_b(const Params& P, Ctx& c, const Task&
   }
   for (int base = t0; base < t1; base += kMaxChunk) {
     if (base != t0) prefetch(base);
-    // this step's row (bf16-exact values staged from kvcur) into its slot
+    // this step's rows (bf16-exact values staged from kvcur) into their
+    // slots: position pos (decode) or pos .. pos + n (prefill).  Fewer than
+    // PPP rows, so each thread holds at most one of them: row `row` in pass
+    // `jn`.
+    const int rel = c.pos - base - pg;
+    const int jn = rel <= 0 ? 0 : (rel + PPP - 1) / PPP;
+    const int row = jn * PPP - rel;  // = position - pos
+    const bool has = jn < NPASS && row <= (pf ? n : 0) && base + jn * PPP + pg < t1;
     uint4 kb, vb;
     {
-      const float4 k0 = *reinterpret_cast<const float4*>(kcur + ds * 8);
-      const float4 k1 = *reinterpret_cast<const float4*>(kcur + ds * 8 + 4);
-      const float4 v0 = *reinterpret_cast<const float4*>(vcur + ds * 8);
-      const float4 v1 = *reinterpret_cast<const float4*>(vcur + ds * 8 + 4);
+      const int rr = has ? row : 0;
+      const float4 k0 = *reinterpret_cast<const float4*>(kcur + rr * D + ds * 8);
+      const float4 k1 = *reinterpret_cast<const float4*>(kcur + rr * D + ds * 8 + 4);
+      const float4 v0 = *reinterpret_cast<const float4*>(vcur + rr * D + ds * 8);
+      const float4 v1 = *reinterpret_cast<const float4*>(vcur + rr * D + ds * 8 + 4);
       kb = {pack_bf16x2(k0.x, k0.y), pack_bf16x2(k0.z, k0.w), pack_bf16x2(k1.x, k1.y), pack_bf16x2(k1.z, k1.w)};
       vb = {pack_bf16x2(v0.x, v0.y), pack_bf16x2(v0.z, v0.w), pack_bf16x2(v1.x, v1.y), pack_bf16x2(v1.z, v1.w)};
     }
 #pragma unroll
     for (int j = 0; j < NPASS; ++j) {
-      const bool here = base + j * PPP + pg == c.pos;
+      const bool here = has && j == jn;
       kr[j].x = here ? kb.x : kr[j].x;
       kr[j].y = here ? kb.y : kr[j].y;
       kr[j].z = here ? kb.z : kr[j].z;

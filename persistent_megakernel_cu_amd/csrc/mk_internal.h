@@ -178,6 +178,7 @@ struct Params {
   uint32_t epoch;
   const StepArgs* dargs; // non-null: read pos and epoch from here (graph mode)
   int32_t partial;       // the plan has partial-input down-projection tasks (selects the kernel instance)
+  int32_t prefill;       // batched plans: the B "sequences" are tokens pos .. pos + B - 1 of one sequence
   // multi-step launches: step i's greedy tokens are published as 64-bit words
   // (epoch of step i + 1 in the high half, the token in the low half) that
   // step i + 1 polls before its first stage; the full epoch cannot match a

@@ -92,6 +92,9 @@ int plan_build(const mk_config& c, int W, Plan& p) {
   if (c.partial_input && (p.batched || p.D != 64))
     return fail(p, MK_E_UNSUPPORTED, "partial-input starts need batch 1 and head_dim 64");
   p.partial = c.partial_input != 0;
+  if (c.prefill && (!p.batched || c.exec_mode > MK_MODE_GRAPH))
+    return fail(p, MK_E_UNSUPPORTED, "prefill needs batch 2..8 and a megakernel mode");
+  p.prefill = c.prefill != 0;
   if (p.batched && (p.Hp > kChunkCols || p.QDp > kChunkCols))
     return fail(p, MK_E_UNSUPPORTED, "batched decode needs hidden and n_heads * head_dim <= 2048");
 
@@ -269,7 +272,9 @@ int plan_build(const mk_config& c, int W, Plan& p) {
   // ---- LDS layout
   // attention scratch: q [G][D], k and v of this step [D] each, per-wave
   // partial outputs [waves][G][D], per-wave max and sum [waves][G] each
-  const int attn_floats = p.G * p.D + 2 * p.D + kWaves * p.G * p.D + 2 * kWaves * p.G;
+  // (prefill: the k and v rows of all B tokens of the step)
+  const int kv_rows = p.prefill ? p.B : 1;
+  const int attn_floats = p.G * p.D + 2 * kv_rows * p.D + kWaves * p.G * p.D + 2 * kWaves * p.G;
   if (p.batched) {
     p.act_stride = std::max(std::max(p.Hp, p.QDp), std::min(p.Fp, kChunkCols));
     p.act_floats = round_up(std::max(p.B * p.act_stride, attn_floats), 4);
@@ -283,7 +288,7 @@ int plan_build(const mk_config& c, int W, Plan& p) {
   p.lds_act = kRingBytes;
   p.lds_res = p.lds_act + p.act_floats * 4;
   p.lds_rope = p.lds_res + p.res_floats * 4;
-  p.lds_misc = p.lds_rope + round_up(p.D, 4) * 4;
+  p.lds_misc = p.lds_rope + round_up(p.D * kv_rows, 4) * 4;  // cos/sin of each token's position
   p.lds_part = p.lds_misc + 256;
   // split-item sums; batched: one 16x16 fp32 tile per wave
   p.lds_tape = p.lds_part + std::max(kMaxItems, kWaves * kTileRows * 16) * 4;

@@ -21,6 +21,7 @@ struct Plan {
   int attn_slices = 1;  // batch 1: attention tasks per (kv head, chunk), one per query head or 1
   bool batched = false;  // B > 1: tiled weights, MFMA tasks
   bool partial = false;  // batch 1: down-projection tasks start on partial input (kRegionPartial)
+  bool prefill = false;  // batched: the B rows are consecutive tokens of one sequence (one KV cache)
   int stages = 0;  // kStagesPerLayer * L + 1
   bool tied = true;
 

@@ -198,3 +198,13 @@ def test_partial_input_plans():
     with pytest.raises(mkb.MkError) as e:
         mkb.plan_describe(LLAMA_8B, 2112, 256, partial_input=True)
     assert e.value.code == mkb.MK_E_UNSUPPORTED
+
+
+def test_prefill_plans():
+    # prefill runs on the batched (MFMA) executors: 2..8 tokens per call, megakernel modes only
+    info = mkb.plan_describe(LLAMA_1B, 256, 256, batch=8, prefill=True)
+    assert info.num_stages == 5 * LLAMA_1B.n_layers + 1 and info.lds_bytes <= 160 * 1024
+    for kw in ({"batch": 1}, {"batch": 4, "mode": "conv"}):
+        with pytest.raises(mkb.MkError) as e:
+            mkb.plan_describe(TINY, 48, 256, prefill=True, **kw)
+        assert e.value.code in (mkb.MK_E_UNSUPPORTED, mkb.MK_E_INVAL)
