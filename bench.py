@@ -9,13 +9,16 @@ and captured) and the CPU oracle.
 
 Default workload (llama1b): 16 layers, hidden 2048, 32 query / 8 KV heads of
 64, SwiGLU 8192, vocab 128256, tied embedding, RoPE theta 5e5, bf16 weights
-~N(0, 0.02) from seed 0.  A 128-token seeded prompt is prefilled through the
+~N(0, 0.02) from seed 0.  A 128-token seeded prompt is run through the
 model (untimed), W warm-up steps run, then K greedy steps are timed from
 position 128 with the token chained on the device (out_token of step i is
-d_token of step i+1).  Other workloads: llama1b-long (single steps at
-positions 4096 and 8191 over a seeded 8192-slot cache, each repeated K
-times) and llama8b (K greedy steps from position 2048 over a seeded cache).
-Prints one JSON line.
+d_token of step i+1).  The headline mode (mega-steps) runs the K timed steps
+in one persistent launch; mega runs one launch per step.  Other workloads:
+llama1b-long (single steps at positions 4096 and 8191 over a seeded
+8192-slot cache, each repeated K times; headline: one launch per step),
+llama1b-b8 (8 sequences) and llama8b (refused by the library for now).
+Extra legs: the prompt as prefill calls against decode steps, and the W2A8
+matrix-vector executor.  Prints one JSON line.
 """
 
 from __future__ import annotations
@@ -32,16 +35,20 @@ sys.path.insert(0, ROOT)
 METRIC = "µs/token batch-1 decode (Llama-1B shape) + achieved HBM GB/s vs 8 TB/s peak"
 HBM_PEAK_GBPS = 8000.0
 
-# HBM bytes per decode step of the megakernel at the llama1b workload, from
-# rocprofv3 FETCH_SIZE / WRITE_SIZE scaled by a 1 GiB copy (the summary and
-# commands are in profiles/mk_persistent_llama1b_hbm_bytes.md).  They describe
-# the kernel sources whose hash is recorded; any other source gives null.
+# HBM bytes per decode step of the megakernel at the llama1b workload, per
+# execution mode, from rocprofv3 FETCH_SIZE / WRITE_SIZE scaled by a 1 GiB
+# copy (summaries and commands: profiles/mk_persistent_llama1b_hbm_bytes.md for
+# one launch per step, profiles/mk_persistent_steps_llama1b.md for all steps in
+# one launch, the launch's counters divided by its steps).  They describe the
+# kernel sources whose hash is recorded; any other source gives null.
 MEASURED_TRAFFIC = {
     "sources_sha256_prefix": "ea74cd1ef05f4b26",
-    "fetch_bytes": 2.5078e9,
-    "write_bytes": 6.139e6,
     "fetch_factor": 2.000,
     "write_factor": 1.000,
+    "per_step": {
+        "mega": {"fetch_bytes": 2.5078e9, "write_bytes": 6.139e6},
+        "mega-steps": {"fetch_bytes": 2.5124e9, "write_bytes": 6.161e6},
+    },
 }
 KERNEL_SOURCES = ("csrc/mk_device.h", "csrc/mk_inst.hip", "csrc/mk_kernels.hip", "csrc/mk_internal.h",
                   "csrc/mk_addr.h", "csrc/mk_plan.cpp")
@@ -57,11 +64,12 @@ def kernel_sources_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, mode: str, steps_per_launch: int):
     """HBM bytes per launch from the committed counters, or None when the kernel changed since."""
-    if workload != "llama1b" or kernel_sources_hash() != MEASURED_TRAFFIC["sources_sha256_prefix"]:
+    per = MEASURED_TRAFFIC["per_step"].get(mode)
+    if workload != "llama1b" or per is None or kernel_sources_hash() != MEASURED_TRAFFIC["sources_sha256_prefix"]:
         return None
-    return MEASURED_TRAFFIC["fetch_bytes"] + MEASURED_TRAFFIC["write_bytes"]
+    return (per["fetch_bytes"] + per["write_bytes"]) * steps_per_launch
 
 
 def algorithmic_bytes(shape, pos: int, batch: int = 1) -> int:
@@ -408,8 +416,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=128)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="llama1b")
-    ap.add_argument("--modes", default="mega,graph,multi,conv,conv-graph",
-                    help="mega: the persistent megakernel; graph / multi: its executors one launch per stage, "
+    ap.add_argument("--modes", default="mega-steps,mega,graph,multi,conv,conv-graph",
+                    help="mega-steps: the persistent megakernel running every timed step in one launch "
+                         "(mk_decode_steps); mega: one launch per step; graph / multi: its executors one launch per stage, "
                          "captured or not; conv / conv-graph: the conventional one-kernel-per-operation path, "
                          "eager or captured in a hipGraph; mega-partial: the megakernel with the partial-input "
                          "down projection")
@@ -454,7 +463,13 @@ def main() -> int:
         results[mode], tokens[mode], per_pos[mode] = ms, toks, pp
         print(f"[bench] {mode}: {ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
 
-    main_mode = "mega" if "mega" in results else next(iter(results))
+    # the headline: every timed step in one persistent launch where the
+    # workload chains its steps, else one launch per step
+    if "mega-steps" in results and wl.name != "llama1b-long":
+        main_mode = "mega-steps"
+    else:
+        main_mode = "mega" if "mega" in results else next(iter(results))
+    steps_per_launch = steps if main_mode == "mega-steps" else 1
     ms = results[main_mode]
     B = wl.batch
     us_tok = ms * 1e3 / B
@@ -501,10 +516,13 @@ def main() -> int:
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(args.workload),
+            "traffic": measured_traffic(args.workload, main_mode, steps_per_launch),
             "bytes_per_step": int(avg_bytes),
-            "traffic_unit": "HBM bytes per launch (one launch = one decode step)",
+            "steps_per_launch": steps_per_launch,
+            "bytes_per_launch": int(avg_bytes * steps_per_launch),
+            "traffic_unit": f"HBM bytes per launch ({main_mode}: {steps_per_launch} decode step(s) per launch)",
         },
+        "main_mode": main_mode,
         "baselines": {m: {"us_per_token": round(v * 1e3 / B, 2), "tokens_per_s": round(B * 1e3 / v, 1)}
                       for m, v in results.items()},
         "modes_agree": all(t == tokens[main_mode] for t in tokens.values()),
@@ -512,9 +530,9 @@ def main() -> int:
     if per_pos[main_mode]:
         out["per_position_us"] = {str(p): round(t * 1e3, 2) for p, t in sorted(per_pos[main_mode].items())}
     if "graph" in results and "mega" in results:
-        out["speedup_vs_graph"] = round(results["graph"] / results["mega"], 3)
+        out["speedup_vs_graph"] = round(results["graph"] / results[main_mode], 3)
     if "conv-graph" in results and "mega" in results:
-        out["speedup_vs_conv_graph"] = round(results["conv-graph"] / results["mega"], 3)
+        out["speedup_vs_conv_graph"] = round(results["conv-graph"] / results[main_mode], 3)
     if not args.no_prefill and wl.prompt_len >= 8 and B == 1:
         out["prefill"] = prefill_bench(mk, torch, wl, wdev, max_seq)
         print(f"[bench] prefill: {out['prefill']['prefill_us']} us for {out['prefill']['prompt_tokens']} tokens "
