@@ -458,10 +458,21 @@ def main() -> int:
     print(f"[bench] {wl.name}: weights ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
     results, tokens, per_pos = {}, {}, {}
+    refused = {}
     for mode in args.modes.split(","):
-        ms, toks, pp = time_mode(mk, torch, wl, wdev, mode, args.warmup, steps, max_seq, args.attn_chunks)
+        try:
+            ms, toks, pp = time_mode(mk, torch, wl, wdev, mode, args.warmup, steps, max_seq, args.attn_chunks)
+        except mk.MkError as e:
+            if e.code != mk.MK_E_UNSUPPORTED:
+                raise
+            refused[mode] = mk.error_string(e.code)  # e.g. the megakernel modes at the Llama-8B shape
+            print(f"[bench] {mode}: refused by the library ({refused[mode]})", file=sys.stderr, flush=True)
+            continue
         results[mode], tokens[mode], per_pos[mode] = ms, toks, pp
         print(f"[bench] {mode}: {ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+    if not results:
+        print(json.dumps({"error": f"every mode was refused for workload {wl.name}", "refused": refused}))
+        return 2
 
     # the headline: every timed step in one persistent launch where the
     # workload chains its steps, else one launch per step
@@ -523,6 +534,7 @@ def main() -> int:
             "traffic_unit": f"HBM bytes per launch ({main_mode}: {steps_per_launch} decode step(s) per launch)",
         },
         "main_mode": main_mode,
+        "refused_modes": refused,
         "baselines": {m: {"us_per_token": round(v * 1e3 / B, 2), "tokens_per_s": round(B * 1e3 / v, 1)}
                       for m, v in results.items()},
         "modes_agree": all(t == tokens[main_mode] for t in tokens.values()),

@@ -85,6 +85,47 @@ def test_conv_llama1b_batch8(llama1b):
                                label="conv-llama1b-b8")
 
 
+@pytest.mark.parametrize("mode", ["conv", "conv-graph"])
+def test_conv_tiny_head_dim_128(mode):
+    # head_dim 128 (16 threads per K/V row in attention), untied
+    sh = TINY.with_(head_dim=128, tie_embeddings=False)
+    w = make_weights(sh, master=11, gain_jitter=0.1)
+    run_teacher_forced(sh, w, 48, make_prompt(sh, 8, master=11), 0, 8, mode=mode, label="conv-tiny-d128")
+
+
+def test_conv_llama8b_seeded_cache():
+    # the Llama-8B shape (head_dim 128, hidden 4096, untied LM head) on the
+    # conventional path: two teacher-forced steps at positions 2048 and 2049
+    # over a seeded 2048-slot cache, logits, tokens and cache slots checked
+    import time
+
+    from synth_inputs import LLAMA_8B
+
+    sh = LLAMA_8B
+    t0 = time.time()
+    w = make_weights(sh, master=0)
+    log(f"[conv-8b] weights generated in {time.time() - t0:.0f}s")
+    kv = make_kv_cache(sh, 1, 2112, 2048, master=0)
+    o = orc.Oracle(sh, w, lazy=True)
+    gpu = GpuDecoder(sh, w, 2112, mode="conv", kv_init=kv)
+    log(f"[conv-8b] engine loaded at {time.time() - t0:.0f}s")
+    kc, vc = kv[0][0].copy(), kv[1][0].copy()
+    tok = make_start_token(sh, 0)
+    try:
+        for pos in (2048, 2049):
+            before = gpu.cache_np()
+            lg, out = gpu.step(tok, pos)
+            after = gpu.cache_np()
+            log(f"[conv-8b] gpu step at {pos} done at {time.time() - t0:.0f}s")
+            lg_ref = o.decode_step(tok, pos, kc, vc)
+            rep = check_step(pos, lg, out, lg_ref, before, after, (kc, vc))
+            log(f"[parity] conv llama8b pos={pos} err/tol={rep.max_abs_err / rep.tol:.3g} at {time.time() - t0:.0f}s")
+            assert out == rep.oracle_token or rep.margin < rep.tol
+            tok = rep.oracle_token
+    finally:
+        gpu.close()
+
+
 def test_conv_bad_token(tiny_w):
     gpu = GpuDecoder(TINY, tiny_w, 48, mode="conv")
     try:
