@@ -1391,13 +1391,12 @@ __device__ __forceinline__ int token_of(const Params& P, const Ctx& c, int n, in
 }
 
 // RMSNorm of the staged batch: wave n < B computes rs[n] = (mean(x^2) +
-// eps)^(-1/2) over x = dst[n][0, H) and scales dst[n][k] by g[k] (zeroing
-// [H, Hp)), so that W . rmsnorm(x_n) = rs[n] * (W . dst_n).
-__device__ __forceinline__ void norm_batch(const Params& P, Ctx& c, float* dst, int stride, const float* g,
+// eps)^(-1/2) over x = dst[n][0, H) and scales dst[n][k] by the gain gl[k]
+// (zeroing [H, Hp)), so that W . rmsnorm(x_n) = rs[n] * (W . dst_n).  The
+// gains gl[0, H) are already in LDS (staged with the activation).
+__device__ __forceinline__ void norm_batch(const Params& P, Ctx& c, float* dst, int stride, const float* gl,
                                            float* rsb) {
-  // lane: 4 consecutive columns per step of 256 (H and Hp are multiples of 4);
-  // the gains of 4 steps are loaded before their LDS updates, so global loads
-  // are not serialised behind LDS stores
+  // lane: 4 consecutive columns per step of 256 (H and Hp are multiples of 4)
   if (c.wave < P.B) {
     float* x = dst + c.wave * stride;
     float ss = 0.f;
@@ -1407,23 +1406,16 @@ __device__ __forceinline__ void norm_batch(const Params& P, Ctx& c, float* dst, 
     }
     ss = wave_sum(ss);
     if (c.lane == 0) rsb[c.wave] = rsqrtf(ss / (float)P.H + P.eps);
-    for (int k0 = c.lane * 4; k0 < P.Hp; k0 += 4 * 256) {
-      float4 gv[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int k = k0 + u * 256;
-        gv[u] = k < P.H ? *reinterpret_cast<const float4*>(g + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = c.lane * 4; k < P.Hp; k += 256) {
+      // padding columns [H, Hp) become zero whatever they held
+      float4 v = *reinterpret_cast<float4*>(x + k);
+      if (k < P.H) {
+        const float4 gv = *reinterpret_cast<const float4*>(gl + k);
+        v = make_float4(v.x * gv.x, v.y * gv.y, v.z * gv.z, v.w * gv.w);
+      } else {
+        v = make_float4(0.f, 0.f, 0.f, 0.f);
       }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int k = k0 + u * 256;
-        if (k < P.Hp) {  // padding columns [H, Hp) become zero whatever they held
-          float4 v = *reinterpret_cast<const float4*>(x + k);
-          v = k < P.H ? make_float4(v.x * gv[u].x, v.y * gv[u].y, v.z * gv[u].z, v.w * gv[u].w)
-                      : make_float4(0.f, 0.f, 0.f, 0.f);
-          *reinterpret_cast<float4*>(x + k) = v;
-        }
-      }
+      *reinterpret_cast<float4*>(x + k) = v;
     }
   }
   __syncthreads();
@@ -1583,10 +1575,15 @@ __device__ __forceinline__ bool gemm_task(const Params& P, Ctx& c, Stream& st, c
 
   // ---- prologue: first chunk of the activation, norms, residual rows, RoPE
   if (OP == OP_QKV || OP == OP_GU || OP == OP_LM) {
-    // cos/sin of this step's position, or (prefill) of each token's position
+    // cos/sin of this step's position, or (prefill) of each token's position,
+    // and the norm gains (H <= 2048: four per thread): loaded before the
+    // activation's first poll round, so that they arrive with it rather than
+    // behind the weight loads the waves issue meanwhile
     const int nrope = P.prefill ? P.B * P.D : P.D;
     float rv = 0.f;
     if (OP == OP_QKV && c.tid < nrope) rv = P.rope[addr::rope_row(c.pos + c.tid / P.D, P.D) + c.tid % P.D];
+    const float* g = OP == OP_QKV ? P.g_attn + (size_t)l * P.Hp : OP == OP_GU ? P.g_ffn + (size_t)l * P.Hp : P.g_final;
+    const float4 gv = 4 * c.tid < P.H ? *reinterpret_cast<const float4*>(g + 4 * c.tid) : make_float4(0.f, 0.f, 0.f, 0.f);
     if (OP == OP_QKV && l == 0) {
       // embedding rows of the batch's tokens
       __syncthreads();
@@ -1601,9 +1598,12 @@ __device__ __forceinline__ bool gemm_task(const Params& P, Ctx& c, Stream& st, c
                                         : P.x_ffn + (size_t)(OP == OP_LM ? P.L - 1 : l - 1) * P.H;
       if (!stage_batch(P, c, c.act, stride, src, (size_t)P.L * P.H, 0, P.H, P.H, s)) return false;
     }
-    const float* g = OP == OP_QKV ? P.g_attn + (size_t)l * P.Hp : OP == OP_GU ? P.g_ffn + (size_t)l * P.Hp : P.g_final;
+    // the gains into the split-part area (free until this task's MFMA loop
+    // ends; the staging above ended with a barrier)
+    if (4 * c.tid < P.H) *reinterpret_cast<float4*>(c.part + 4 * c.tid) = gv;
     if (OP == OP_QKV && c.tid < nrope) c.rope[c.tid] = rv;
-    norm_batch(P, c, c.act, stride, g, rsb);
+    __syncthreads();
+    norm_batch(P, c, c.act, stride, c.part, rsb);
   } else {
     // residual rows [r0, r0 + nr) of every sequence, then the activation
     const int r0 = (int)t.a0 * kTileRows, nr = nblk * kTileRows;
