@@ -116,7 +116,40 @@ __device__ __forceinline__ tword ready_word(uint32_t epoch, uint32_t v_bits = 0u
 // is simply polled again.
 typedef uint32_t tword4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const volatile tword4 gtword4;
+// Two scopes for the same four words.  The volatile 16-byte load is issued at
+// system scope (sc0 sc1) and is the faster one for the batch-1 path's small
+// stagings (one 16-byte group per thread), which are latency-bound.  The
+// batched path stages the activations of every sequence (up to 64 KB per
+// workgroup, every workgroup at once) and is bound by the fabric's throughput
+// for coherent loads; there the agent-scope load (sc1 alone: bypasses this
+// XCD's L2, whose copy of a line that another XCD rewrote may be stale) moves
+// the same bytes faster: 1328 -> 1211 us per 8-sequence step.
 __device__ __forceinline__ tword4 ld_tag4(const tword* p) { return *(gtword4*)p; }
+// Cache-policy operand of a gfx950 buffer load that sets sc1 alone (agent scope).
+constexpr int kCachePolicyAgent = 16;
+// Fourth word of a raw (untyped, unswizzled) gfx9 buffer resource.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+// A buffer resource over the words [base, base + bytes / 4) (base wave-uniform).
+// An offset past the range reads zeros: a wrong tag, polled until the watchdog
+// stops the kernel, never a fault.
+struct TagBuf {
+  __amdgpu_buffer_rsrc_t r;
+};
+__device__ __forceinline__ TagBuf tag_buf(const tword* base, uint32_t bytes) {
+  return TagBuf{__builtin_amdgcn_make_buffer_rsrc(const_cast<tword*>(base), (short)0, (int)bytes, kBufferRsrcWord3)};
+}
+// Four tagged words at word offset `word` of the resource, at agent scope.
+__device__ __forceinline__ tword4 ld_tag4_agent(const TagBuf& b, uint32_t word) {
+  return __builtin_amdgcn_raw_buffer_load_b128(b.r, (int)(word * 4u), 0, kCachePolicyAgent);
+}
+// Four tagged words at p at agent scope, as two 8-byte atomic loads (for
+// per-thread addresses that no single resource covers).
+__device__ __forceinline__ tword4 ld_tag4_agent(const tword* p) {
+  uint64_t* q = reinterpret_cast<uint64_t*>(const_cast<tword*>(p));
+  const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return tword4{(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32)};
+}
 __device__ __forceinline__ bool tag4_ready(tword4 w, uint32_t epoch) {
   return ((((w.x ^ epoch) | (w.y ^ epoch) | (w.z ^ epoch) | (w.w ^ epoch)) & 0xFFu) == 0);
 }
@@ -1328,6 +1361,8 @@ __device__ __forceinline__ bool stage_batch(const Params& P, Ctx& c, float* dst,
                                             size_t sstride, int k0, int kc, int kpad, int stage) {
   // groups of 4 columns (kc, k0, sstride and stride are multiples of 4)
   const int total = P.B * kc;
+  // every group read below lies in [base, base + (B - 1) sstride + k0 + kc)
+  const TagBuf tb = tag_buf(base, (uint32_t)(((size_t)(P.B - 1) * sstride + k0 + kc) * 4));
   bool stop = false;
   for (int i0 = 0; i0 == 0 || i0 < total; i0 += 4 * kThreads * kStageLoadsBatch) {
     tword4 w[kStageLoadsBatch];
@@ -1335,7 +1370,7 @@ __device__ __forceinline__ bool stage_batch(const Params& P, Ctx& c, float* dst,
     for (int j = 0; j < kStageLoadsBatch; ++j) {
       const int i = i0 + 4 * (j * kThreads + c.tid);
       const int n = i < total ? i / kc : 0, k = i - n * kc;
-      w[j] = i < total ? ld_tag4(base + (size_t)n * sstride + k0 + k) : ready_word4(c.epoch);
+      w[j] = i < total ? ld_tag4_agent(tb, (uint32_t)((size_t)n * sstride + k0 + k)) : ready_word4(c.epoch);
     }
     uint64_t t0 = 0;
     while (!stop) {
@@ -1352,7 +1387,7 @@ __device__ __forceinline__ bool stage_batch(const Params& P, Ctx& c, float* dst,
         const int i = i0 + 4 * (j * kThreads + c.tid);
         if (i < total && !tag4_ready(w[j], c.epoch)) {
           const int n = i / kc, k = i - n * kc;
-          w[j] = ld_tag4(base + (size_t)n * sstride + k0 + k);
+          w[j] = ld_tag4_agent(tb, (uint32_t)((size_t)n * sstride + k0 + k));
         }
       }
     }
@@ -1806,7 +1841,7 @@ __device__ __forceinline__ bool stage_prefill_qkv(const Params& P, Ctx& c, int l
     dst = (r < D ? kcur : vcur) + m * D + (r % D);
     scale = 1.f;
   }
-  tword4 w = on ? ld_tag4(src) : ready_word4(c.epoch);
+  tword4 w = on ? ld_tag4_agent(src) : ready_word4(c.epoch);
   uint64_t t0 = 0;
   bool stop = false;
   while (!tag4_ready(w, c.epoch)) {
@@ -1814,7 +1849,7 @@ __device__ __forceinline__ bool stage_prefill_qkv(const Params& P, Ctx& c, int l
       stop = true;
       break;
     }
-    w = ld_tag4(src);
+    w = ld_tag4_agent(src);
   }
   __syncthreads();  // the previous task's LDS readers are done
   if (on && !stop) {

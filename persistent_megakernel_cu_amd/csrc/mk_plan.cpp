@@ -333,6 +333,11 @@ int plan_validate(const Plan& p, std::string* why) {
   };
   const int W = p.W;
   if ((int)p.tape.size() != p.stages * W) return bad("tape size");
+  {
+    // the batched staging addresses a tagged buffer with 32-bit byte offsets
+    const Workspace w = layout_workspace(p);
+    if (w.kpart.off + w.kpart.bytes - w.x_attn.off >= (1ull << 31)) return bad("tagged activations exceed 2 GiB");
+  }
   for (int s = 0; s < p.stages; ++s) {
     const bool lm = s == p.stages - 1;
     const int kind = lm ? OP_LM : 1 + (s % kStagesPerLayer);
