@@ -174,7 +174,8 @@ typedef struct mk_plan_info {
   int64_t weight_bytes;   /* bytes of the packed weight arena               */
   int64_t workspace_bytes;/* bytes of activations, flags, tape, tables      */
   int32_t lds_bytes;      /* dynamic LDS per workgroup                      */
-  int32_t reserved[5];
+  int32_t ring_units;     /* 1 KiB weight units each wave keeps in flight   */
+  int32_t reserved[4];
 } mk_plan_info;
 
 typedef struct mk_handle mk_handle;

@@ -74,7 +74,7 @@ class MkPlanInfo(ctypes.Structure):
     _fields_ = [("num_wgs", ctypes.c_int32), ("num_stages", ctypes.c_int32), ("num_tasks", ctypes.c_int32),
                 ("attn_chunks", ctypes.c_int32), ("weight_bytes", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_int64), ("lds_bytes", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 5)]
+                ("ring_units", ctypes.c_int32), ("reserved", ctypes.c_int32 * 4)]
 
 
 class MkError(RuntimeError):

@@ -326,6 +326,7 @@ int mk_plan_describe(const mk_config* cfg, int32_t num_wgs, mk_plan_info* out) {
   out->weight_bytes = (int64_t)(p.arena_bytes + p.lm_bytes);
   out->workspace_bytes = (int64_t)layout_workspace(p).bytes + (int64_t)p.tape.size() * 32;
   out->lds_bytes = p.lds_bytes;
+  out->ring_units = p.ring_units;
   return MK_OK;
 }
 
@@ -362,6 +363,11 @@ int mk_load(const mk_config* cfg, const mk_weights* w, mk_handle** out) {
   // more are refused until the cause is known.  Such plans still build and
   // validate on the host.
   if (p.D != 64 || p.H > 2048 || p.arena_bytes + p.lm_bytes >= (4ull << 30)) {
+    release(h);
+    return MK_E_UNSUPPORTED;
+  }
+  // the kernels' rings are kRing (batch 1) or kRingBatched units deep
+  if (p.ring_units != (p.batched ? mk::kRingBatched : mk::kRing)) {
     release(h);
     return MK_E_UNSUPPORTED;
   }

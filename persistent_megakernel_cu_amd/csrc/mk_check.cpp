@@ -254,7 +254,7 @@ extern "C" int mkcheck_walk(const mk_config* cfg, int num_wgs, int pos, long lon
   const Workspace ws = layout_workspace(p);
   Walker w(p, pos, slack);
   // LDS regions in order, inside the 160 KiB of a workgroup
-  w.rule(kRingBytes <= p.lds_act && p.lds_act + 4 * p.act_floats <= p.lds_res && p.lds_res + 4 * p.res_floats <= p.lds_rope &&
+  w.rule(ring_bytes(p.ring_units) <= p.lds_act && p.lds_act + 4 * p.act_floats <= p.lds_res && p.lds_res + 4 * p.res_floats <= p.lds_rope &&
              p.lds_rope + 4 * p.D <= p.lds_misc && p.lds_misc + 256 <= p.lds_part && p.lds_tape + p.stages * 32 <= p.lds_bytes &&
              p.lds_bytes <= 160 * 1024,
          "LDS layout");

@@ -1310,7 +1310,7 @@ __device__ __forceinline__ void loader_issue_b(const Params& P, Stream& st, int 
   const char* g = st.lbase + ((uint64_t)block * st.lnu + kb) * kUnitBytes + (uint32_t)lane * 16u;
   dma_unit(g, st.ring + (uint32_t)st.lslot * kUnitBytes);
   ++st.issued;
-  st.lslot = (st.lslot + 1 == kRing) ? 0 : st.lslot + 1;
+  st.lslot = (st.lslot + 1 == kRingBatched) ? 0 : st.lslot + 1;
   if (++st.lu == st.lupi) {
     st.lu = 0;
     st.litem += kWaves;
@@ -1322,33 +1322,33 @@ __device__ __forceinline__ void loader_issue_b(const Params& P, Stream& st, int 
 }
 
 __device__ __forceinline__ void top_up_b(const Params& P, Stream& st, int wave, int lane, int max) {
-  while (max-- > 0 && !st.ldone && st.issued - st.consumed < kRing) loader_issue_b(P, st, wave, lane);
+  while (max-- > 0 && !st.ldone && st.issued - st.consumed < kRingBatched) loader_issue_b(P, st, wave, lane);
 }
 
 // Next four tiles of the stream (all issued: the ring is refilled on consume).
 __device__ __forceinline__ void take4_b(const Params& P, Stream& st, int wave, int lane, uint4 (&v)[4]) {
-  if (st.issued - st.consumed == kRing)
-    wait_vm<kRing - 4>();
+  if (st.issued - st.consumed == kRingBatched)
+    wait_vm<kRingBatched - 4>();
   else
     wait_vm<0>();
   uint32_t a[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     int sl = st.cslot + k;
-    sl = sl >= kRing ? sl - kRing : sl;
+    sl = sl >= kRingBatched ? sl - kRingBatched : sl;
     a[k] = st.ring + (uint32_t)sl * kUnitBytes + (uint32_t)lane * 16u;
   }
   lds_read4(v, a);
   st.consumed += 4;
-  st.cslot = st.cslot + 4 >= kRing ? st.cslot + 4 - kRing : st.cslot + 4;
+  st.cslot = st.cslot + 4 >= kRingBatched ? st.cslot + 4 - kRingBatched : st.cslot + 4;
   top_up_b(P, st, wave, lane, 4);
 }
 
 __device__ __forceinline__ uint4 take1_b(const Params& P, Stream& st, int wave, int lane) {
   const uint32_t a = st.ring + (uint32_t)st.cslot * kUnitBytes + (uint32_t)lane * 16u;
-  const uint4 v = (st.issued - st.consumed == kRing) ? ring_read<kRing - 1>(a) : ring_read<0>(a);
+  const uint4 v = (st.issued - st.consumed == kRingBatched) ? ring_read<kRingBatched - 1>(a) : ring_read<0>(a);
   ++st.consumed;
-  st.cslot = (st.cslot + 1 == kRing) ? 0 : st.cslot + 1;
+  st.cslot = (st.cslot + 1 == kRingBatched) ? 0 : st.cslot + 1;
   top_up_b(P, st, wave, lane, 1);
   return v;
 }
@@ -2110,7 +2110,7 @@ __device__ __forceinline__ void run_stages(const Params& P, int s_begin, int s_e
   __syncthreads();
 
   Stream st;
-  st.ring = lds_byte(smem) + (uint32_t)c.wave * (uint32_t)(kRing * kUnitBytes);
+  st.ring = lds_byte(smem) + (uint32_t)c.wave * (uint32_t)((BATCHED ? kRingBatched : kRing) * kUnitBytes);
   st.tape = lds_byte(smem) + (uint32_t)P.lds_tape;
   st.issued = st.consumed = st.lslot = st.cslot = 0;
   st.s_begin = s_begin;
@@ -2119,7 +2119,7 @@ __device__ __forceinline__ void run_stages(const Params& P, int s_begin, int s_e
   st.ldone = false;
   if constexpr (BATCHED) {
     loader_seek_b(P, st, s_begin, c.wave);
-    top_up_b(P, st, c.wave, c.lane, kRing);
+    top_up_b(P, st, c.wave, c.lane, kRingBatched);
   } else {
     loader_seek(P, st, s_begin, c.b, c.wave);
     top_up(P, st, c.b, c.wave, c.lane, kRing);

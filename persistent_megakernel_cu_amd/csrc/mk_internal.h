@@ -19,9 +19,15 @@ constexpr int kUnitBytes = 1024;
 constexpr int kUnitElems = kUnitBytes / 2;  // bf16 elements per unit
 // Rows are padded to a multiple of one unit.
 constexpr int kRowAlign = kUnitElems;
-// Per-wave LDS ring of weight units kept in flight (8 KiB per wave, 64 KiB
-// per workgroup).  A compile-time depth keeps every wait count an immediate.
-constexpr int kRing = 8;
+// Per-wave LDS ring of weight units kept in flight: 14 KiB per wave (112 KiB
+// per workgroup) on the batch-1 path, 8 KiB per wave on the batched path,
+// whose activation tiles take more LDS.  Compile-time depths keep every wait
+// count an immediate.  The planner lays out batch-1 plans whose LDS does not
+// fit beside the deep ring with kRingMin, for the host-side description and
+// address walk only: the library refuses to run them.
+constexpr int kRing = 14;
+constexpr int kRingMin = 8;
+constexpr int kRingBatched = 8;
 // Largest group of query heads sharing one KV head.
 constexpr int kMaxGroup = 8;
 // Largest number of split items (pairs << kslog) of one task (LDS partials).
@@ -192,8 +198,8 @@ struct Params {
 // then for each wave the time its first weight unit of the task was in hand.
 constexpr int kTraceStamps = 4 + 2 * kWaves;
 
-// LDS bytes of the per-wave rings.
-constexpr int kRingBytes = kWaves * kRing * kUnitBytes;
+// LDS bytes of the per-wave rings of a given depth.
+constexpr int ring_bytes(int units) { return kWaves * units * kUnitBytes; }
 
 }  // namespace mk
 

@@ -284,15 +284,19 @@ int plan_build(const mk_config& c, int W, Plan& p) {
     p.res_floats = round_up(std::max(max_res_rows, 4), 4);
   }
   if (max_res_rows > kThreads) return fail(p, MK_E_UNSUPPORTED, "more than 512 residual rows per workgroup");
-  p.ring_units = kRing;
-  p.lds_act = kRingBytes;
-  p.lds_res = p.lds_act + p.act_floats * 4;
-  p.lds_rope = p.lds_res + p.res_floats * 4;
-  p.lds_misc = p.lds_rope + round_up(p.D * kv_rows, 4) * 4;  // cos/sin of each token's position
-  p.lds_part = p.lds_misc + 256;
-  // split-item sums; batched: one 16x16 fp32 tile per wave
-  p.lds_tape = p.lds_part + std::max(kMaxItems, kWaves * kTileRows * 16) * 4;
-  p.lds_bytes = p.lds_tape + p.stages * (int)sizeof(Task);
+  auto lay_out = [&](int ring_units) {
+    p.ring_units = ring_units;
+    p.lds_act = ring_bytes(ring_units);
+    p.lds_res = p.lds_act + p.act_floats * 4;
+    p.lds_rope = p.lds_res + p.res_floats * 4;
+    p.lds_misc = p.lds_rope + round_up(p.D * kv_rows, 4) * 4;  // cos/sin of each token's position
+    p.lds_part = p.lds_misc + 256;
+    // split-item sums; batched: one 16x16 fp32 tile per wave
+    p.lds_tape = p.lds_part + std::max(kMaxItems, kWaves * kTileRows * 16) * 4;
+    p.lds_bytes = p.lds_tape + p.stages * (int)sizeof(Task);
+  };
+  lay_out(p.batched ? kRingBatched : kRing);
+  if (!p.batched && p.lds_bytes > 160 * 1024) lay_out(kRingMin);
   if (p.lds_bytes > 160 * 1024) return fail(p, MK_E_UNSUPPORTED, "LDS plan exceeds 160 KiB per workgroup");
   return MK_OK;
 }
@@ -460,6 +464,8 @@ int plan_validate(const Plan& p, std::string* why) {
     if (next != pairs) return bad("row pairs not covered");
   }
   if (p.lds_bytes > 160 * 1024) return bad("LDS");
+  if (p.batched ? p.ring_units != kRingBatched : (p.ring_units != kRing && p.ring_units != kRingMin))
+    return bad("ring depth");
   return MK_OK;
 }
 

@@ -41,6 +41,19 @@ def test_plan_validates(shape, max_seq, chunks):
         assert info.weight_bytes <= shape.n_layers * per_layer + 5 * shape.n_layers * 4096
 
 
+def test_ring_depth_follows_the_lds_budget():
+    # batch-1 plans keep 14 weight units per wave in flight; a plan whose LDS
+    # does not fit beside that ring (the 8B shape's 14336-wide FFN
+    # activation) is laid out with 8 for its description and address walk,
+    # and mk_load refuses it; batched plans keep 8
+    info = mkb.plan_describe(LLAMA_1B, 1088, 256)
+    assert info.ring_units == 14 and info.lds_bytes <= 160 * 1024
+    info = mkb.plan_describe(LLAMA_8B, 2112, 256)
+    assert info.ring_units == 8 and info.lds_bytes <= 160 * 1024
+    assert mkb.plan_describe(LLAMA_1B, 1088, 256, batch=8).ring_units == 8
+    assert mkb.plan_describe(TINY, 48, 256).ring_units == 14
+
+
 @pytest.mark.parametrize("shape,max_seq,batch,chunks", [
     (TINY, 48, 4, 1), (TINY, 48, 8, 1), (LLAMA_1B, 1088, 8, 4), (LLAMA_1B, 256, 2, 1)])
 def test_plan_batched_validates(shape, max_seq, batch, chunks):
