@@ -1456,23 +1456,35 @@ __device__ __forceinline__ void norm_batch(const Params& P, Ctx& c, float* dst, 
   __syncthreads();
 }
 
-// B operand of one tile: lane l holds sequence l % 16 (zero past the batch),
-// columns 8 * (l / 16) .. +8 of the tile, as bf16 hi and lo parts (x = hi +
-// lo to about 16 significant bits), so two MFMAs give an fp32-accurate
-// product with the bf16 weights.
+// B operand of one tile: lane l holds sequence l % 16, columns 8 * (l / 16)
+// .. +8 of the tile, as bf16 hi and lo parts (x = hi + lo to about 16
+// significant bits), so two MFMAs give an fp32-accurate product with the bf16
+// weights.  Lanes past the batch read sequence 0: column n of an MFMA result
+// depends on column n of B alone, and the columns past the batch are never
+// used.  Pairs are rounded together (one packed conversion for two hi parts,
+// one for two lo parts).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void hilo_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const bf16x2 h = __builtin_convertvector(f32x2{x0, x1}, bf16x2);
+  __builtin_memcpy(&hi, &h, sizeof(hi));
+  const float r0 = x0 - __uint_as_float(hi << 16);
+  const float r1 = x1 - __uint_as_float(hi & 0xFFFF0000u);
+  const bf16x2 l = __builtin_convertvector(f32x2{r0, r1}, bf16x2);
+  __builtin_memcpy(&lo, &l, sizeof(lo));
+}
 __device__ __forceinline__ void b_operand(const float* act, int stride, int n, bool live, int col,
                                           bf16x8& hi, bf16x8& lo) {
   const float* x = act + (live ? n : 0) * stride + col;
   const float4 a = *reinterpret_cast<const float4*>(x);
   const float4 b = *reinterpret_cast<const float4*>(x + 4);
-  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float xv = live ? v[i] : 0.f;
-    const __bf16 h = (__bf16)xv;
-    hi[i] = h;
-    lo[i] = (__bf16)(xv - (float)h);
-  }
+  uint4 h, l;
+  hilo_pair(a.x, a.y, h.x, l.x);
+  hilo_pair(a.z, a.w, h.y, l.y);
+  hilo_pair(b.x, b.y, h.z, l.z);
+  hilo_pair(b.z, b.w, h.w, l.w);
+  __builtin_memcpy(&hi, &h, sizeof(hi));
+  __builtin_memcpy(&lo, &l, sizeof(lo));
 }
 
 __device__ __forceinline__ f32x4 mfma_tile(const uint4 w, const bf16x8& hi, const bf16x8& lo, f32x4 acc) {
