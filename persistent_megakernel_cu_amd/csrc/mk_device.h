@@ -1873,11 +1873,48 @@ __device__ __forceinline__ bool stage_prefill_qkv(const Params& P, Ctx& c, int l
   return c.flags[0] == 0;
 }
 
+// Eight bf16 of a row held in LDS as bf16-exact fp32 (this step's k or v rows).
+__device__ __forceinline__ uint4 pack8_bf16(const float* x) {
+  const float4 a = *reinterpret_cast<const float4*>(x);
+  const float4 b = *reinterpret_cast<const float4*>(x + 4);
+  return make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w));
+}
+
+// Eight fp32 in LDS as the bf16 hi and lo parts of an MFMA operand.
+__device__ __forceinline__ void hilo8_lds(const float* x, bf16x8& hi, bf16x8& lo) {
+  const float4 a = *reinterpret_cast<const float4*>(x);
+  const float4 b = *reinterpret_cast<const float4*>(x + 4);
+  uint4 h, l;
+  hilo_pair(a.x, a.y, h.x, l.x);
+  hilo_pair(a.z, a.w, h.y, l.y);
+  hilo_pair(b.x, b.y, h.z, l.z);
+  hilo_pair(b.z, b.w, h.w, l.w);
+  __builtin_memcpy(&hi, &h, sizeof(hi));
+  __builtin_memcpy(&lo, &l, sizeof(lo));
+}
+
+// Batched attention on MFMA: task (sequence nu, kv head a0, chunk a1); the
+// chunk's positions are cut into blocks of 32, block q walked by wave q % 8,
+// each wave keeping the running maximum, sum and P.V of the G query heads.
+// Per block, in the 16x16x32 bf16 MFMA layout (A: lane l holds row l % 16,
+// k elements 8 (l / 16) .. +8; B: column l % 16, same k; C: column l % 16,
+// rows 4 (l / 16) .. +4):
+//   scores S^T[position][head] = K . Q^T: A = two 16-position tiles of K rows
+//     (bf16, straight from the cache), B = q in bf16 hi and lo parts, two
+//     halves of head_dim 64 (8 MFMAs);
+//   softmax per head over the 4 lanes holding its column;
+//   O[head][d] += P . V: A = P rows (hi and lo) read back from a per-wave LDS
+//     scratch, B = V transposed through a per-wave LDS scratch (rows of 32
+//     positions, 80 bytes apart), four 16-wide d tiles (8 MFMAs).
+// Positions from pos on take this step's k and v rows from LDS; positions past
+// the chunk are masked.  The eight waves' {max, sum, P.V} are then merged as
+// in attn_task.
 template <int G, int D>
 __device__ __forceinline__ bool attn_task_b(const Params& P, Ctx& c, const Task& t, int s) {
-  constexpr int NT = D / 8;
-  constexpr int PPP = kThreads / NT;
-  constexpr int NPASS = kMaxChunk / PPP;
+  static_assert(D == 64, "batched attention: head_dim 64 (two 32-wide MFMA k halves)");
+  static_assert(G <= 4, "batched attention: the P.V rows of all heads in one lane group");
+  constexpr int BLK = 32;  // positions per block
+  constexpr int VRS = 40;  // V^T row stride in bf16 (32 positions, 8 padding)
   const int l = t.layer, g = (int)t.a0, ch = (int)t.a1, n = (int)t.nu;
   const int C = P.attn_chunks;
   // prefill: token n of one sequence, at position pos + n, sees the cache
@@ -1886,24 +1923,38 @@ __device__ __forceinline__ bool attn_task_b(const Params& P, Ctx& c, const Task&
   const int npos = c.pos + (pf ? n : 0) + 1;
   const int len0 = (npos + C - 1) / C;
   const int t0 = min(npos, ch * len0), t1 = min(npos, t0 + len0);
+  const int nblk = (t1 - t0 + BLK - 1) / BLK;
 
   const size_t head_off = (seq_off(P, pf ? 0 : n, l, P.NKV) + g) * P.S * D;
-  const int ds = c.tid % NT;
-  const int pg = c.tid / NT;
-  uint4 kr[NPASS], vr[NPASS];
-  auto prefetch = [&](int base) {
+  const int r16 = c.lane & 15, q4 = c.lane >> 4;  // MFMA lane roles
+  // V rows: lane loads position vp of the block, the 8-wide d chunks 2 j + vh
+  // (j < 4), so that its transposed writes and the other half-wave's fall on
+  // different LDS banks
+  const int vp = c.lane & 31, vh = c.lane >> 5;
+  // K and V of one block from the cache: positions from pos on (this step's,
+  // from LDS below) and past the chunk read slot 0 (in bounds)
+  uint4 kq[2][2], vq[4];
+  auto load_block = [&](int base) {
 #pragma unroll
-    for (int j = 0; j < NPASS; ++j) {
-      const int tp = base + j * PPP + pg;
-      // slots from pos on are this step's (staged below); slot 0 stands in
-      const int tl = (tp < t1 && tp < c.pos) ? tp : 0;
-      const size_t o = head_off + (size_t)tl * D + ds * 8;
-      kr[j] = *reinterpret_cast<const uint4*>(P.kcache + o);
-      vr[j] = *reinterpret_cast<const uint4*>(P.vcache + o);
+    for (int mt = 0; mt < 2; ++mt) {
+      const int p = base + 16 * mt + r16;
+      const int sl = (p < t1 && p < c.pos) ? p : 0;
+      const uint16_t* kr = P.kcache + head_off + (size_t)sl * D + 8 * q4;
+      kq[mt][0] = *reinterpret_cast<const uint4*>(kr);
+      kq[mt][1] = *reinterpret_cast<const uint4*>(kr + 32);
     }
+    const int p = base + vp;
+    const int sl = (p < t1 && p < c.pos) ? p : 0;
+    const uint16_t* vr = P.vcache + head_off + (size_t)sl * D + 8 * vh;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vq[j] = *reinterpret_cast<const uint4*>(vr + 16 * j);
   };
-  prefetch(t0);
+  const int blk0 = c.wave;
+  if (blk0 < nblk) load_block(t0 + blk0 * BLK);
 
+  // LDS: q [G][D] (scaled), this step's k and v rows [nrows][D], per-wave
+  // partial outputs [waves][G][D], per-wave max and sum [waves][G], then per
+  // wave the block's probabilities [G][32] and V^T [D][VRS] bf16
   const int nrows = pf ? P.B : 1;  // k / v rows of this step in LDS
   float* qs = c.act;
   float* kcur = qs + G * D;
@@ -1911,6 +1962,8 @@ __device__ __forceinline__ bool attn_task_b(const Params& P, Ctx& c, const Task&
   float* wpart = vcur + nrows * D;
   float* wm = wpart + kWaves * G * D;
   float* wl = wm + kWaves * G;
+  float* pw = wl + kWaves * G + c.wave * (G * BLK + D * VRS / 2);
+  uint16_t* vt = reinterpret_cast<uint16_t*>(pw + G * BLK);
   if (!pf) {
     const Seg seg[3] = {{qs, P.q + seq_off(P, n, l, P.QD) + (size_t)g * G * D, G * D, P.qscale},
                         {kcur, P.kvcur + seq_off(P, n, l, 2 * P.KVD) + (size_t)g * D, D, 1.f},
@@ -1920,102 +1973,132 @@ __device__ __forceinline__ bool attn_task_b(const Params& P, Ctx& c, const Task&
     return false;
   }
   mark(c, 1);
-  float acc[G][8], ls[G], m[G];
+
+  // q as the B operand: lane: head r16 (zero past G), dims 8 q4 + 32 dh .. +8
+  bf16x8 qh[2], ql[2];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    ls[h] = 0.f;
-    m[h] = -__builtin_inff();
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  for (int dh = 0; dh < 2; ++dh) {
+    hilo8_lds(qs + (r16 < G ? r16 : 0) * D + 8 * q4 + 32 * dh, qh[dh], ql[dh]);
+    if (r16 >= G) {
+      qh[dh] = bf16x8{};
+      ql[dh] = bf16x8{};
+    }
   }
-  for (int base = t0; base < t1; base += kMaxChunk) {
-    if (base != t0) prefetch(base);
-    // this step's rows (bf16-exact values staged from kvcur) into their
-    // slots: position pos (decode) or pos .. pos + n (prefill).  Fewer than
-    // PPP rows, so each thread holds at most one of them: row `row` in pass
-    // `jn`.
-    const int rel = c.pos - base - pg;
-    const int jn = rel <= 0 ? 0 : (rel + PPP - 1) / PPP;
-    const int row = jn * PPP - rel;  // = position - pos
-    const bool has = jn < NPASS && row <= (pf ? n : 0) && base + jn * PPP + pg < t1;
-    uint4 kb, vb;
+  float m = -__builtin_inff(), ls = 0.f;  // softmax state of head r16 (its 4 lanes agree)
+  f32x4 ov[4];                            // O[head 4 q4 + i][d = r16 + 16 dt]
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) ov[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int q = blk0; q < nblk; q += kWaves) {
+    const int base = t0 + q * BLK;
+    if (q != blk0) load_block(base);
+    // this step's rows (bf16-exact values in LDS) for the positions from pos on
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int p = base + 16 * mt + r16;
+      if (p >= c.pos && p < t1) {
+        const float* kr = kcur + (p - c.pos) * D + 8 * q4;
+        kq[mt][0] = pack8_bf16(kr);
+        kq[mt][1] = pack8_bf16(kr + 32);
+      }
+    }
     {
-      const int rr = has ? row : 0;
-      const float4 k0 = *reinterpret_cast<const float4*>(kcur + rr * D + ds * 8);
-      const float4 k1 = *reinterpret_cast<const float4*>(kcur + rr * D + ds * 8 + 4);
-      const float4 v0 = *reinterpret_cast<const float4*>(vcur + rr * D + ds * 8);
-      const float4 v1 = *reinterpret_cast<const float4*>(vcur + rr * D + ds * 8 + 4);
-      kb = {pack_bf16x2(k0.x, k0.y), pack_bf16x2(k0.z, k0.w), pack_bf16x2(k1.x, k1.y), pack_bf16x2(k1.z, k1.w)};
-      vb = {pack_bf16x2(v0.x, v0.y), pack_bf16x2(v0.z, v0.w), pack_bf16x2(v1.x, v1.y), pack_bf16x2(v1.z, v1.w)};
-    }
+      const int p = base + vp;
+      if (p >= c.pos && p < t1) {
 #pragma unroll
-    for (int j = 0; j < NPASS; ++j) {
-      const bool here = has && j == jn;
-      kr[j].x = here ? kb.x : kr[j].x;
-      kr[j].y = here ? kb.y : kr[j].y;
-      kr[j].z = here ? kb.z : kr[j].z;
-      kr[j].w = here ? kb.w : kr[j].w;
-      vr[j].x = here ? vb.x : vr[j].x;
-      vr[j].y = here ? vb.y : vr[j].y;
-      vr[j].z = here ? vb.z : vr[j].z;
-      vr[j].w = here ? vb.w : vr[j].w;
-    }
+        for (int j = 0; j < 4; ++j) vq[j] = pack8_bf16(vcur + (p - c.pos) * D + 8 * vh + 16 * j);
+      } else if (p >= t1) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float4 qa = *reinterpret_cast<const float4*>(qs + h * D + ds * 8);
-      const float4 qb = *reinterpret_cast<const float4*>(qs + h * D + ds * 8 + 4);
-      float sc[NPASS];
-      float mb = -__builtin_inff();
-#pragma unroll
-      for (int j = 0; j < NPASS; ++j) {
-        const float a = slice_sum<NT>(dot8r(kr[j], qa, qb));
-        sc[j] = base + j * PPP + pg < t1 ? a : -__builtin_inff();
-        mb = fmaxf(mb, sc[j]);
-      }
-      mb = wave_max(mb);
-      const float mn = fmaxf(m[h], mb);
-      const float scale = m[h] == -__builtin_inff() ? 0.f : __expf(m[h] - mn);
-      ls[h] *= scale;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] *= scale;
-      m[h] = mn;
-#pragma unroll
-      for (int j = 0; j < NPASS; ++j) {
-        const float p = sc[j] == -__builtin_inff() ? 0.f : __expf(sc[j] - mn);
-        ls[h] += p;
-        const uint4 w = vr[j];
-        acc[h][0] = fmaf(p, bf_lo(w.x), acc[h][0]);
-        acc[h][1] = fmaf(p, bf_hi(w.x), acc[h][1]);
-        acc[h][2] = fmaf(p, bf_lo(w.y), acc[h][2]);
-        acc[h][3] = fmaf(p, bf_hi(w.y), acc[h][3]);
-        acc[h][4] = fmaf(p, bf_lo(w.z), acc[h][4]);
-        acc[h][5] = fmaf(p, bf_hi(w.z), acc[h][5]);
-        acc[h][6] = fmaf(p, bf_lo(w.w), acc[h][6]);
-        acc[h][7] = fmaf(p, bf_hi(w.w), acc[h][7]);
+        for (int j = 0; j < 4; ++j) vq[j] = make_uint4(0u, 0u, 0u, 0u);
       }
     }
-  }
-  float wsum[G];
+    // scores of the two 16-position tiles
+    f32x4 sc[2];
+    float bm = -__builtin_inff();
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    wsum[h] = wave_sum(ds == 0 ? ls[h] : 0.f);
+    for (int mt = 0; mt < 2; ++mt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = group_sum<NT>(acc[h][e]);
-  }
-  if (c.lane < NT) {
+      for (int dh = 0; dh < 2; ++dh) {
+        bf16x8 a;
+        __builtin_memcpy(&a, &kq[mt][dh], sizeof(a));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[dh], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[dh], acc, 0, 0, 0);
+      }
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float* dst = wpart + (c.wave * G + h) * D + ds * 8;
-      *reinterpret_cast<float4*>(dst) = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-      *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+      for (int i = 0; i < 4; ++i) {
+        const int p = base + 16 * mt + 4 * q4 + i;
+        acc[i] = (p < t1 && r16 < G) ? acc[i] : -__builtin_inff();
+        bm = fmaxf(bm, acc[i]);
+      }
+      sc[mt] = acc;
     }
-  }
-  if (c.lane == 0) {
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float mn = fmaxf(m, bm);
+    const float scale = m == -__builtin_inff() ? 0.f : __expf(m - mn);
+    float ps = 0.f;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      wm[c.wave * G + h] = m[h];
-      wl[c.wave * G + h] = wsum[h];
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e = sc[mt][i] == -__builtin_inff() ? 0.f : __expf(sc[mt][i] - mn);
+        sc[mt][i] = e;
+        ps += e;
+      }
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    ls = fmaf(ls, scale, ps);
+    m = mn;
+    // P rows to LDS: lane: head r16, positions 16 mt + 4 q4 .. +4
+    if (r16 < G) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        *reinterpret_cast<f32x4*>(pw + r16 * BLK + 16 * mt + 4 * q4) = sc[mt];
     }
+    // V^T: position vp, dims 8 (2 j + vh) .. +8
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w4[4] = {vq[j].x, vq[j].y, vq[j].z, vq[j].w};
+      uint16_t* col = vt + (8 * (2 * j + vh)) * VRS + vp;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) col[e * VRS] = (uint16_t)((e & 1) ? (w4[e >> 1] >> 16) : (w4[e >> 1] & 0xFFFFu));
+    }
+    __builtin_amdgcn_wave_barrier();
+    // the rows of O are rescaled by their head's factor (heads 0..3: lanes 0..3)
+    float sh[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sh[i] = lane_value(scale, i);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ov[dt][i] *= sh[i];
+    // P as the A operand: lane: head r16 (zero past G), positions 8 q4 .. +8
+    bf16x8 ph, pl;
+    hilo8_lds(pw + (r16 < G ? r16 : 0) * BLK + 8 * q4, ph, pl);
+    if (r16 >= G) {
+      ph = bf16x8{};
+      pl = bf16x8{};
+    }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const uint4 vb4 = *reinterpret_cast<const uint4*>(vt + (r16 + 16 * dt) * VRS + 8 * q4);
+      bf16x8 vb;
+      __builtin_memcpy(&vb, &vb4, sizeof(vb));
+      ov[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vb, ov[dt], 0, 0, 0);
+      ov[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, ov[dt], 0, 0, 0);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  // this wave's {max, sum} (lanes 0..G-1) and P.V rows (lanes 0..15: heads i < G)
+  if (q4 == 0) {
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) wpart[(c.wave * G + i) * D + r16 + 16 * dt] = ov[dt][i];
+  }
+  if (c.lane < G) {
+    wm[c.wave * G + c.lane] = m;
+    wl[c.wave * G + c.lane] = ls;
   }
   mark_wave(c);
   __syncthreads();

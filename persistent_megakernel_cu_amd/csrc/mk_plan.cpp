@@ -272,9 +272,11 @@ int plan_build(const mk_config& c, int W, Plan& p) {
   // ---- LDS layout
   // attention scratch: q [G][D], k and v of this step [D] each, per-wave
   // partial outputs [waves][G][D], per-wave max and sum [waves][G] each
-  // (prefill: the k and v rows of all B tokens of the step)
+  // (prefill: the k and v rows of all B tokens of the step); batched plans
+  // add per wave the MFMA path's probabilities [G][32] and V^T [D][40] bf16
   const int kv_rows = p.prefill ? p.B : 1;
-  const int attn_floats = p.G * p.D + 2 * kv_rows * p.D + kWaves * p.G * p.D + 2 * kWaves * p.G;
+  const int attn_floats = p.G * p.D + 2 * kv_rows * p.D + kWaves * p.G * p.D + 2 * kWaves * p.G +
+                          (p.batched ? kWaves * (p.G * 32 + p.D * 20) : 0);
   if (p.batched) {
     p.act_stride = std::max(std::max(p.Hp, p.QDp), std::min(p.Fp, kChunkCols));
     p.act_floats = round_up(std::max(p.B * p.act_stride, attn_floats), 4);

@@ -250,6 +250,16 @@ def test_tiny_batched_untied_chunked():
     run_batched_teacher_forced(sh, w, 48, prompts, 0, 4, mode="mega", attn_chunks=4, label="tiny-b3-untied")
 
 
+def test_tiny_batched_long_chunks(tiny_w):
+    # 2 sequences over seeded 4000-slot caches, attention in 2 chunks of ~2000
+    # positions: every wave walks about eight 32-position blocks, carrying its
+    # softmax maximum, sum and P.V from block to block
+    kv = make_kv_cache(TINY, 2, 4100, 4000, master=6)
+    starts = [[make_start_token(TINY, n)] for n in range(2)]
+    run_batched_teacher_forced(TINY, tiny_w, 4100, starts, 4000, 3, mode="mega", kv_init=kv, attn_chunks=2,
+                               label="tiny-b2-long")
+
+
 def test_llama1b_batch8_seeded_cache(llama1b):
     # batch 8 over seeded 1024-slot caches (attention chunks walked in blocks):
     # the start tokens at position 1024, then 8 greedy steps, every sequence
