@@ -1049,19 +1049,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // maximum first, then the rescaled sums, in chunk order.  Thread tid < GT * D
 // owns output element tid.  The {m, l} table goes through LDS (2 * C * GT
 // floats at tab); the accumulators are loaded KG chunks at a time into
-// registers, all KG loads in flight together, the first KG issued before the
-// table loads, so a merge costs ceil(C / KG) memory round trips instead of
-// one per chunk.  Called by the whole workgroup (one barrier).
-template <int GT, int D, int KG>
+// registers, all KG loads in flight together, and with EARLY the first KG
+// issued before the table loads, so a merge costs ceil(C / KG) (EARLY) or 1 +
+// ceil(C / KG) memory round trips instead of one per chunk (the batched path
+// measured faster without EARLY).  Called by the whole workgroup (one barrier).
+template <int GT, int D, int KG, bool EARLY>
 __device__ __forceinline__ void merge_chunks(const Ctx& c, const float* base, int C, int stride, int GQ,
                                              int h0, float* tab, tword* o) {
   const bool mine = c.tid < GT * D;
   const int h = c.tid / D;
   float av[KG];
-  // the first KG chunks' accumulators are in flight with the table loads
+  // EARLY: the first KG chunks' accumulators are in flight with the table loads
+  if (EARLY) {
 #pragma unroll
-  for (int u = 0; u < KG; ++u)
-    av[u] = (mine && u < C) ? ld_f32_agent(base + (size_t)u * stride + 2 * GQ + h0 * D + c.tid) : 0.f;
+    for (int u = 0; u < KG; ++u)
+      av[u] = (mine && u < C) ? ld_f32_agent(base + (size_t)u * stride + 2 * GQ + h0 * D + c.tid) : 0.f;
+  }
   for (int i = c.tid; i < C * GT; i += kThreads) {
     const int k = i / GT, hh = i - k * GT;
     const float* pk = base + (size_t)k * stride + h0 + hh;
@@ -1074,7 +1077,7 @@ __device__ __forceinline__ void merge_chunks(const Ctx& c, const float* base, in
   for (int k = 0; k < C; ++k) MM = fmaxf(MM, tab[2 * (k * GT + h)]);
   float LL = 0.f, AA = 0.f;
   for (int k0 = 0; k0 < C; k0 += KG) {
-    if (k0 > 0) {
+    if (!EARLY || k0 > 0) {
 #pragma unroll
       for (int u = 0; u < KG; ++u)
         av[u] = k0 + u < C ? ld_f32_agent(base + (size_t)(k0 + u) * stride + 2 * GQ + h0 * D + c.tid) : 0.f;
@@ -1258,7 +1261,7 @@ __device__ __forceinline__ bool attn_task(const Params& P, Ctx& c, const Task& t
   // the {m, l} table reuses wpart (free after the barrier above):
   // 2 * C * GT <= kWaves * GT * D because C <= 256 <= 4 * D
   if (c.flags[1])
-    merge_chunks<GT, D, 32>(c, P.attn_part + addr::attn_rec(l, P.NKV, g, C, 0, stride), C, stride, GQ, hq0, wpart, o);
+    merge_chunks<GT, D, 32, true>(c, P.attn_part + addr::attn_rec(l, P.NKV, g, C, 0, stride), C, stride, GQ, hq0, wpart, o);
   return true;
 }
 
@@ -2143,7 +2146,7 @@ __device__ __forceinline__ bool attn_task_b(const Params& P, Ctx& c, const Task&
     c.flags[1] = old == c.epoch * (uint32_t)C - 1u;
   }
   __syncthreads();
-  if (c.flags[1]) merge_chunks<G, D, 8>(c, P.attn_part + head * C * stride, C, stride, G, 0, wpart, o);
+  if (c.flags[1]) merge_chunks<G, D, 8, false>(c, P.attn_part + head * C * stride, C, stride, G, 0, wpart, o);
   return true;
 }
 

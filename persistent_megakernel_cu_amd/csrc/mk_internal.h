@@ -27,7 +27,7 @@ constexpr int kRowAlign = kUnitElems;
 // address walk only: the library refuses to run them.
 constexpr int kRing = 14;
 constexpr int kRingMin = 8;
-constexpr int kRingBatched = 8;
+constexpr int kRingBatched = 10;
 // Largest group of query heads sharing one KV head.
 constexpr int kMaxGroup = 8;
 // Largest number of split items (pairs << kslog) of one task (LDS partials).
