@@ -1362,12 +1362,29 @@ __device__ __forceinline__ uint4 take1_b(const Params& P, Stream& st, int wave, 
   return v;
 }
 
+// First round of stage_batch's loads (groups i = 4 (j * 512 + tid) of the B
+// sequences' columns [k0, k0 + kc)), issued ahead of the staging itself.
+__device__ __forceinline__ void stage_batch_issue(const Params& P, const Ctx& c, const tword* base, size_t sstride,
+                                                  int k0, int kc, tword4 (&w)[kStageLoadsBatch]) {
+  const int total = P.B * kc;
+  // every group read lies in [base, base + (B - 1) sstride + k0 + kc)
+  const TagBuf tb = tag_buf(base, (uint32_t)(((size_t)(P.B - 1) * sstride + k0 + kc) * 4));
+#pragma unroll
+  for (int j = 0; j < kStageLoadsBatch; ++j) {
+    const int i = 4 * (j * kThreads + c.tid);
+    const int n = i < total ? i / kc : 0, k = i - n * kc;
+    w[j] = i < total ? ld_tag4_agent(tb, (uint32_t)((size_t)n * sstride + k0 + k)) : ready_word4(c.epoch);
+  }
+}
+
 // Stage columns [k0, k0 + kc) of B tagged sequences into LDS:
 // dst[n * stride + k] = src_n[k0 + k], src_n = base + n * sstride.  The first
 // round's loads are in flight before the barrier that separates these LDS
-// writes from the previous task's reads.  Ends with a barrier.
+// writes from the previous task's reads; `pre`, if given, holds that round's
+// words already loaded by stage_batch_issue.  Ends with a barrier.
 __device__ __forceinline__ bool stage_batch(const Params& P, Ctx& c, float* dst, int stride, const tword* base,
-                                            size_t sstride, int k0, int kc, int kpad, int stage) {
+                                            size_t sstride, int k0, int kc, int kpad, int stage,
+                                            const tword4 (*pre)[kStageLoadsBatch] = nullptr) {
   // groups of 4 columns (kc, k0, sstride and stride are multiples of 4)
   const int total = P.B * kc;
   // every group read below lies in [base, base + (B - 1) sstride + k0 + kc)
@@ -1375,11 +1392,16 @@ __device__ __forceinline__ bool stage_batch(const Params& P, Ctx& c, float* dst,
   bool stop = false;
   for (int i0 = 0; i0 == 0 || i0 < total; i0 += 4 * kThreads * kStageLoadsBatch) {
     tword4 w[kStageLoadsBatch];
+    if (pre != nullptr && i0 == 0) {
 #pragma unroll
-    for (int j = 0; j < kStageLoadsBatch; ++j) {
-      const int i = i0 + 4 * (j * kThreads + c.tid);
-      const int n = i < total ? i / kc : 0, k = i - n * kc;
-      w[j] = i < total ? ld_tag4_agent(tb, (uint32_t)((size_t)n * sstride + k0 + k)) : ready_word4(c.epoch);
+      for (int j = 0; j < kStageLoadsBatch; ++j) w[j] = (*pre)[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < kStageLoadsBatch; ++j) {
+        const int i = i0 + 4 * (j * kThreads + c.tid);
+        const int n = i < total ? i / kc : 0, k = i - n * kc;
+        w[j] = i < total ? ld_tag4_agent(tb, (uint32_t)((size_t)n * sstride + k0 + k)) : ready_word4(c.epoch);
+      }
     }
     uint64_t t0 = 0;
     while (!stop) {
@@ -1702,13 +1724,23 @@ __device__ __forceinline__ bool gemm_task(const Params& P, Ctx& c, Stream& st, c
   const int kq = (c.lane >> 4) * 8;
   LmBestB best{-__builtin_inff(), -1};
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // a later chunk's first round of loads is issued before the MFMA loop of
+  // the chunk before it, so its round trip overlaps that chunk's compute
+  tword4 wn[kStageLoadsBatch];
   for (int cc = cb; cc < ce; ++cc) {
-    if (cc > cb) {  // next chunk of the activation (one item per wave: acc carries over)
+    if constexpr (OP == OP_OPROJ || OP == OP_DOWN) {  // the others have one chunk (H <= 2048)
       const tword* src = OP == OP_OPROJ ? P.o + addr::layer_off(l, P.QD) : P.h + addr::layer_off(l, P.F);
       const int kfull = OP == OP_OPROJ ? P.QD : P.F;
-      const int kcc = max(0, min(ch * kTileCols, kfull - cc * ch * kTileCols));
-      if (!stage_batch(P, c, c.act, stride, src, (size_t)P.L * kfull, cc * ch * kTileCols, kcc, ch * kTileCols, s))
-        return false;
+      if (cc > cb) {  // next chunk of the activation (one item per wave: acc carries over)
+        const int kcc = max(0, min(ch * kTileCols, kfull - cc * ch * kTileCols));
+        if (!stage_batch(P, c, c.act, stride, src, (size_t)P.L * kfull, cc * ch * kTileCols, kcc, ch * kTileCols, s,
+                         &wn))
+          return false;
+      }
+      if (cc + 1 < ce) {
+        const int kcn = max(0, min(ch * kTileCols, kfull - (cc + 1) * ch * kTileCols));
+        stage_batch_issue(P, c, src, (size_t)P.L * kfull, (cc + 1) * ch * kTileCols, kcn, wn);
+      }
     }
     for (int i = c.wave; i < nitems; i += kWaves) {
       if (nc == 1) acc = f32x4{0.f, 0.f, 0.f, 0.f};
