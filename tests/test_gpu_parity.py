@@ -235,6 +235,24 @@ def test_large_arena_refused():
     assert e.value.code == mkb.MK_E_UNSUPPORTED
 
 
+def test_shallow_ring_plan_refused():
+    # a batch-1 plan whose LDS does not fit beside the 14-unit weight ring (a
+    # 14336-wide FFN activation) is described with 8 units and refused by
+    # mk_load before any weight is read: the kernels carry the 14-unit ring
+    import torch
+
+    from persistent_megakernel_cu_amd import binding as mkb
+    from synth_inputs import weight_shapes
+
+    sh = TINY.with_(ffn=14336)
+    assert mkb.plan_describe(sh, 48).ring_units == 8
+    dummy = torch.zeros(16, dtype=torch.int16, device="cuda")
+    w = {name: dummy for name, _, _ in weight_shapes(sh)}
+    with pytest.raises(mkb.MkError) as e:
+        mkb.Engine(sh, w, 48)
+    assert e.value.code == mkb.MK_E_UNSUPPORTED
+
+
 @pytest.mark.parametrize("mode", ["mega", "multi", "graph"])
 def test_tiny_batched(tiny_w, mode):
     # 4 sequences with their own prompts, tiled weights and MFMA
