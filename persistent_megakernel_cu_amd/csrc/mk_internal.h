@@ -20,7 +20,7 @@ constexpr int kUnitElems = kUnitBytes / 2;  // bf16 elements per unit
 // Rows are padded to a multiple of one unit.
 constexpr int kRowAlign = kUnitElems;
 // Per-wave LDS ring of weight units kept in flight: 14 KiB per wave (112 KiB
-// per workgroup) on the batch-1 path, 8 KiB per wave on the batched path,
+// per workgroup) on the batch-1 path, 10 KiB per wave on the batched path,
 // whose activation tiles take more LDS.  Compile-time depths keep every wait
 // count an immediate.  The planner lays out batch-1 plans whose LDS does not
 // fit beside the deep ring with kRingMin, for the host-side description and
