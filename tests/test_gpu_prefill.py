@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 class Prefiller:
     """A prefill handle (batch = chunk tokens of one sequence) and that sequence's cache."""
 
-    def __init__(self, shape, weights_np, max_seq, chunk, mode="mega", kv_init=None, wd=None):
+    def __init__(self, shape, weights_np, max_seq, chunk, mode="mega", kv_init=None, wd=None, attn_chunks=0):
         import torch
 
         from persistent_megakernel_cu_amd import binding as mkb
@@ -28,7 +28,7 @@ class Prefiller:
         self.torch = torch
         self.T = chunk
         self.wd = wd if wd is not None else mkb.to_device(weights_np)
-        self.eng = mkb.Engine(shape, self.wd, max_seq, mode=mode, batch=chunk, prefill=True)
+        self.eng = mkb.Engine(shape, self.wd, max_seq, mode=mode, batch=chunk, prefill=True, attn_chunks=attn_chunks)
         dims = (1, shape.n_layers, shape.n_kv_heads, max_seq, shape.head_dim)
         if kv_init is None:
             self.k = torch.zeros(dims, dtype=torch.int16, device="cuda")
@@ -74,7 +74,7 @@ def check_chunk(pos, T, lg, out, lg_refs, before, after, ref_cache):
     return worst
 
 
-def run_prefill(shape, w, max_seq, prompt, start, chunk, mode="mega", o=None, kv_init=None, label=""):
+def run_prefill(shape, w, max_seq, prompt, start, chunk, mode="mega", o=None, kv_init=None, label="", attn_chunks=0):
     """Prefill ``prompt`` from ``start`` in calls of ``chunk`` tokens, each
     compared with the oracle's step-by-step run; returns the prefiller (open)
     and the oracle's cache after the prompt."""
@@ -83,7 +83,7 @@ def run_prefill(shape, w, max_seq, prompt, start, chunk, mode="mega", o=None, kv
         kc, vc = o.new_cache(max_seq)
     else:
         kc, vc = kv_init[0][0].copy(), kv_init[1][0].copy()
-    pf = Prefiller(shape, w, max_seq, chunk, mode=mode, kv_init=kv_init)
+    pf = Prefiller(shape, w, max_seq, chunk, mode=mode, kv_init=kv_init, attn_chunks=attn_chunks)
     worst = 0.0
     assert len(prompt) % chunk == 0
     lg_refs = []
@@ -117,6 +117,16 @@ def test_tiny_prefill_chunk_sizes_over_a_seeded_cache(tiny_w, chunk):
     kv = make_kv_cache(TINY, 1, 600, 20, master=4)
     pf, _, _ = run_prefill(TINY, tiny_w, 600, list(make_prompt(TINY, 16, master=4)), 20, chunk, kv_init=kv,
                            label=f"tiny-seeded-c{chunk}")
+    pf.close()
+
+
+def test_tiny_prefill_over_a_long_cache(tiny_w):
+    # a seeded 4000-slot cache, 8-token prefill calls from position 4000, 2
+    # attention chunks of ~2000 positions: every wave walks several 32-position
+    # blocks, and the last block mixes cached slots with the call's own rows
+    kv = make_kv_cache(TINY, 1, 4100, 4000, master=9)
+    pf, _, _ = run_prefill(TINY, tiny_w, 4100, list(make_prompt(TINY, 16, master=9)), 4000, 8, kv_init=kv,
+                           label="tiny-long-c8", attn_chunks=2)
     pf.close()
 
 
