@@ -35,19 +35,30 @@ sys.path.insert(0, ROOT)
 METRIC = "µs/token batch-1 decode (Llama-1B shape) + achieved HBM GB/s vs 8 TB/s peak"
 HBM_PEAK_GBPS = 8000.0
 
-# HBM bytes per decode step of the megakernel at the llama1b workload, per
-# execution mode, from rocprofv3 FETCH_SIZE / WRITE_SIZE scaled by a 1 GiB
-# copy (summaries and commands: profiles/mk_persistent_llama1b_hbm_bytes.md for
-# one launch per step, profiles/mk_persistent_steps_llama1b.md for all steps in
-# one launch, the launch's counters divided by its steps).  They describe the
+# HBM bytes per decode step of the megakernel, per workload and execution
+# mode, from rocprofv3 FETCH_SIZE / WRITE_SIZE scaled by a 1 GiB copy
+# (summaries and commands: profiles/mk_persistent_llama1b_hbm_bytes.md for
+# the batch-1 workloads, profiles/mk_persistent_steps_llama1b.md for all
+# steps in one launch, profiles/mk_persistent_llama1b_b8_kernel_trace.md for
+# 8 sequences; a multi-step launch's counters are divided by its steps, the
+# long-context figure is the mean of its two positions).  They describe the
 # kernel sources whose hash is recorded; any other source gives null.
 MEASURED_TRAFFIC = {
     "sources_sha256_prefix": "5518045bd79f77af",
     "fetch_factor": 2.000,
     "write_factor": 1.000,
     "per_step": {
-        "mega": {"fetch_bytes": 2.5088e9, "write_bytes": 6.430e6},
-        "mega-steps": {"fetch_bytes": 2.5139e9, "write_bytes": 6.449e6},
+        "llama1b": {
+            "mega": {"fetch_bytes": 2.5088e9, "write_bytes": 6.430e6},
+            "mega-steps": {"fetch_bytes": 2.5139e9, "write_bytes": 6.449e6},
+        },
+        "llama1b-long": {
+            "mega": {"fetch_bytes": 2.6990e9, "write_bytes": 1.180e7},
+        },
+        "llama1b-b8": {
+            "mega": {"fetch_bytes": 2.8305e9, "write_bytes": 2.259e7},
+            "mega-steps": {"fetch_bytes": 2.8325e9, "write_bytes": 2.259e7},
+        },
     },
 }
 KERNEL_SOURCES = ("csrc/mk_device.h", "csrc/mk_inst.hip", "csrc/mk_kernels.hip", "csrc/mk_internal.h",
@@ -66,8 +77,8 @@ def kernel_sources_hash() -> str:
 
 def measured_traffic(workload: str, mode: str, steps_per_launch: int):
     """HBM bytes per launch from the committed counters, or None when the kernel changed since."""
-    per = MEASURED_TRAFFIC["per_step"].get(mode)
-    if workload != "llama1b" or per is None or kernel_sources_hash() != MEASURED_TRAFFIC["sources_sha256_prefix"]:
+    per = MEASURED_TRAFFIC["per_step"].get(workload, {}).get(mode)
+    if per is None or kernel_sources_hash() != MEASURED_TRAFFIC["sources_sha256_prefix"]:
         return None
     return (per["fetch_bytes"] + per["write_bytes"]) * steps_per_launch
 
