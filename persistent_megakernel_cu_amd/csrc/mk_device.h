@@ -50,6 +50,11 @@ __device__ __forceinline__ uint32_t lds_byte(const void* p) { return (uint32_t)(
 // One 16-byte-per-lane asynchronous load of global memory into LDS at
 // m0 + 16 * lane.  Issued from inline assembly so that the compiler does not
 // see it: it would otherwise wait for every such load before any LDS read.
+// Non-temporal (nt): every weight byte is read once per step, and a stream
+// of several GB per step would otherwise keep evicting from the L2 what is
+// read again soon: the kernel's code (larger than the instruction cache,
+// refetched at every stage), the activations that every workgroup of an XCD
+// stages, and the KV rows.
 __device__ __forceinline__ void dma_unit(const char* gsrc, uint32_t lds_dst) {
   uint32_t keep;
   lds_dst = __builtin_amdgcn_readfirstlane(lds_dst);
@@ -57,7 +62,7 @@ __device__ __forceinline__ void dma_unit(const char* gsrc, uint32_t lds_dst) {
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
+      "global_load_lds_dwordx4 %1, off nt\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(keep)
       : "v"(gsrc), "s"(lds_dst)
