@@ -11,6 +11,8 @@
 
 #include <algorithm>
 #include <cstring>
+#include <utility>
+#include <vector>
 
 namespace mk {
 
@@ -141,19 +143,29 @@ int plan_build(const mk_config& c, int W, Plan& p) {
   p.stages = kStagesPerLayer * p.L + 1;
   p.tape.assign((size_t)p.stages * W, Task{});
   int max_res_rows = 0;
+  // Which workgroup streams which part of a matrix.  Workgroup b runs on XCD
+  // b mod 8.  The gate/up stage streams 256 KB per workgroup (batch 1: 32 row
+  // pairs of 8 KB; batched: 4 blocks of 64 KB); measured on MI355X, the
+  // whole step is 6-8 us faster when workgroup i of the stage takes range
+  // i + 1 (or i + 5) instead of range i, and 7-8 us slower with i + 3 (i + 2,
+  // i + 4, ... change nothing; the same offsets on the other stages change
+  // nothing either): the 256 KB granules of the weight arena are not equally
+  // near to every XCD.
+  auto range_rotation = [&](Op op, int nw) { return op == OP_GU && nw > 1 ? 1 : 0; };
   // Row pairs of a GEMV stage in contiguous, balanced ranges over workgroups
-  // [b0, W).
+  // [b0, W), range (i + rotation) mod nw on workgroup b0 + i.
   auto gemv_stage = [&](int s, Op op, int layer, uint64_t pairs, uint32_t nu, uint64_t wofs, uint8_t region,
                         int b0 = 0) {
     const int nw = W - b0;
+    const int rot = range_rotation(op, nw);
     uint32_t n = 0;
     for (int i = 0; i < nw; ++i) {
       uint64_t a0 = pairs * (uint64_t)i / nw, a1 = pairs * (uint64_t)(i + 1) / nw;
       if (a1 > a0) ++n;
     }
     for (int i = 0; i < nw; ++i) {
-      const int b = b0 + i;
-      uint64_t a0 = pairs * (uint64_t)i / nw, a1 = pairs * (uint64_t)(i + 1) / nw;
+      const int b = b0 + i, j = (i + rot) % nw;
+      uint64_t a0 = pairs * (uint64_t)j / nw, a1 = pairs * (uint64_t)(j + 1) / nw;
       Task& t = p.tape[(size_t)s * W + b];
       if (a1 == a0) continue;
       t.op = op;
@@ -211,8 +223,10 @@ int plan_build(const mk_config& c, int W, Plan& p) {
     }
     uint32_t n = 0;
     for (int i = 0; i < nw; ++i) n += blocks * (uint64_t)(i + 1) / nw > blocks * (uint64_t)i / nw;
+    const int rot = range_rotation(op, nw);
     for (int i = 0; i < nw; ++i) {
-      const uint64_t a0 = blocks * (uint64_t)i / nw, a1 = blocks * (uint64_t)(i + 1) / nw;
+      const int j = (i + rot) % nw;
+      const uint64_t a0 = blocks * (uint64_t)j / nw, a1 = blocks * (uint64_t)(j + 1) / nw;
       if (a1 == a0) continue;
       Task& t = p.tape[(size_t)s * W + b0 + i];
       t.op = op;
@@ -332,6 +346,17 @@ Workspace layout_workspace(const Plan& p) {
   return w;
 }
 
+// True when the half-open ranges cover [0, total) exactly once.
+static bool tiles_exactly(std::vector<std::pair<uint64_t, uint64_t>> r, uint64_t total) {
+  std::sort(r.begin(), r.end());
+  uint64_t next = 0;
+  for (const auto& x : r) {
+    if (x.first != next || x.second <= x.first) return false;
+    next = x.second;
+  }
+  return next == total;
+}
+
 int plan_validate(const Plan& p, std::string* why) {
   auto bad = [&](const std::string& m) {
     if (why) *why = m;
@@ -398,6 +423,7 @@ int plan_validate(const Plan& p, std::string* why) {
       }
       const uint64_t ch = std::min<uint64_t>(kt, kChunkTiles);
       uint64_t next = 0;
+      std::vector<std::pair<uint64_t, uint64_t>> whole;  // unsplit blocks' ranges, in any workgroup order
       int half0 = -1;  // workgroup holding the first half of a split block, until its second half
       for (int b = 0; b < W; ++b) {
         const Task& t = p.tape[(size_t)s * W + b];
@@ -420,8 +446,8 @@ int plan_validate(const Plan& p, std::string* why) {
           }
         } else {
           if (half0 >= 0) return bad("split block without its second half");
-          if (t.a0 != next || t.a1 <= t.a0) return bad("row blocks not tiled exactly");
-          next = t.a1;
+          if (t.a1 <= t.a0) return bad("row blocks not tiled exactly");
+          whole.push_back({t.a0, t.a1});
         }
         if (t.nu != kt || t.wofs != wofs) return bad("task geometry");
         if ((uint64_t)t.a1 * kt * kUnitBytes > region_bytes) return bad("task reads past its matrix");
@@ -435,17 +461,19 @@ int plan_validate(const Plan& p, std::string* why) {
           return bad("residual rows exceed LDS");
       }
       if (half0 >= 0) return bad("split block without its second half");
-      if (next != rows / kTileRows) return bad("row blocks not covered");
+      if (!whole.empty() && next != 0) return bad("split and unsplit blocks in one stage");
+      if (!whole.empty() && !tiles_exactly(whole, rows / kTileRows)) return bad("row blocks not tiled exactly");
+      if (whole.empty() && next != rows / kTileRows) return bad("row blocks not covered");
       continue;
     }
-    // GEMV: ranges must tile [0, pairs) exactly, in workgroup order
-    uint64_t next = 0;
+    // GEMV: ranges must tile [0, pairs) exactly (in any workgroup order)
+    std::vector<std::pair<uint64_t, uint64_t>> ranges;
     for (int b = 0; b < W; ++b) {
       const Task& t = p.tape[(size_t)s * W + b];
       if (t.op == OP_NONE) continue;
       if (t.op != kind || t.layer != layer) return bad("stage holds another op");
-      if (t.a0 != next || t.a1 <= t.a0) return bad("row pairs not tiled exactly");
-      next = t.a1;
+      if (t.a1 <= t.a0) return bad("row pairs not tiled exactly");
+      ranges.push_back({t.a0, t.a1});
       if (t.nu != nu || t.wofs != wofs) return bad("task geometry");
       if ((uint64_t)t.a1 * t.nu * kUnitBytes > region_bytes) return bad("task reads past its matrix");
       if (t.ntasks != count) return bad("task count");
@@ -463,7 +491,7 @@ int plan_validate(const Plan& p, std::string* why) {
         if ((uint64_t)(t.a1 - t.a0) * ks > (uint64_t)kMaxItems) return bad("too many split items");
       }
     }
-    if (next != pairs) return bad("row pairs not covered");
+    if (!tiles_exactly(ranges, pairs)) return bad("row pairs not tiled exactly");
   }
   if (p.lds_bytes > 160 * 1024) return bad("LDS");
   if (p.batched ? p.ring_units != kRingBatched : (p.ring_units != kRing && p.ring_units != kRingMin))
