@@ -26,10 +26,17 @@ int fail(Plan& p, int code, const char* msg) {
   return code;
 }
 
-// Split of each row pair into 2^k items so that the 8 waves of a workgroup
-// share `pairs` pairs of nu units evenly: minimise the units of the busiest
-// wave, prefer fewer splits on ties.  Items must stay inside one row.
+// Split of each row pair into 2^k items shared by the 8 waves of a
+// workgroup.  One item per row (k = 1) whenever every wave gets at least one
+// row and the items fit the partial-sum area: measured on MI355X against the
+// split that minimises the units of the busiest wave, rows were faster for
+// every Llama-1B stage (gate/up: rows against whole pairs -18 us per step,
+// against half rows -21, against quarter rows -63; QKV: rows against half
+// rows -3 us; O-proj and down: rows against whole pairs -9 / -60 us, against
+// half rows -7 / -5 us).  Otherwise minimise the units of the busiest wave,
+// fewer splits on ties.  Items must stay inside one row.
 uint32_t split_log2(uint32_t pairs, uint32_t nu) {
+  if (nu >= 2 && 2ull * pairs >= (uint64_t)kWaves && 2ull * pairs <= (uint64_t)kMaxItems) return 1;
   uint32_t best = 0;
   uint64_t best_cost = ~0ull;
   for (uint32_t k = 0; (1u << k) <= nu; ++k) {
