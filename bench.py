@@ -44,20 +44,20 @@ HBM_PEAK_GBPS = 8000.0
 # long-context figure is the mean of its two positions).  They describe the
 # kernel sources whose hash is recorded; any other source gives null.
 MEASURED_TRAFFIC = {
-    "sources_sha256_prefix": "ddf2a586d8332ee0",
+    "sources_sha256_prefix": "28f9edfff933cbbd",
     "fetch_factor": 2.000,
     "write_factor": 1.000,
     "per_step": {
         "llama1b": {
-            "mega": {"fetch_bytes": 2.5079e9, "write_bytes": 5.991e6},
-            "mega-steps": {"fetch_bytes": 2.5118e9, "write_bytes": 5.993e6},
+            "mega": {"fetch_bytes": 2.5057e9, "write_bytes": 2.320e6},
+            "mega-steps": {"fetch_bytes": 2.5095e9, "write_bytes": 2.324e6},
         },
         "llama1b-long": {
-            "mega": {"fetch_bytes": 2.6981e9, "write_bytes": 1.137e7},
+            "mega": {"fetch_bytes": 2.6961e9, "write_bytes": 7.696e6},
         },
         "llama1b-b8": {
-            "mega": {"fetch_bytes": 2.8208e9, "write_bytes": 2.241e7},
-            "mega-steps": {"fetch_bytes": 2.8203e9, "write_bytes": 2.241e7},
+            "mega": {"fetch_bytes": 2.8203e9, "write_bytes": 2.241e7},
+            "mega-steps": {"fetch_bytes": 2.8198e9, "write_bytes": 2.241e7},
         },
     },
 }
