@@ -139,7 +139,7 @@ void walk_gemv(Walker& w, const Task& t, const Workspace& ws, uint64_t region_by
       }
     }
   w.rule(units == (uint64_t)(t.a1 - t.a0) * t.nu, "stream covers the task's units once");
-  if (t.kslog > 0) w.in("LDS split partials", 0, n_items, (uint64_t)std::max(kMaxItems, kWaves * kTileRows * 16));
+  if (t.kslog > 0) w.in("LDS split partials", 0, n_items, (uint64_t)std::max(kMaxItems, kWaves * kTileRows * kTileLd));
   if (partial) {
     // down_partial: each wave stages only its columns of h
     for (int wave = 0; wave < kWaves && (uint32_t)wave < n_items; ++wave) {

@@ -42,6 +42,10 @@ constexpr int kMaxChunk = 256;
 // 8 * (l / 16) .. +8); activations of the batch form the B operand.
 constexpr int kMaxBatch = 8;
 constexpr int kTileRows = 16;
+// LDS row stride (floats) of a split item's [row][sequence] partial tile:
+// one past the 16 sequence columns, so that reads along the rows do not
+// fall on one bank.
+constexpr int kTileLd = 17;
 constexpr int kTileCols = 32;
 // Columns of an activation chunk held in LDS at once (per sequence).
 constexpr int kChunkCols = 2048;

@@ -315,7 +315,7 @@ int plan_build(const mk_config& c, int W, Plan& p) {
     p.lds_misc = p.lds_rope + round_up(p.D * kv_rows, 4) * 4;  // cos/sin of each token's position
     p.lds_part = p.lds_misc + 256;
     // split-item sums; batched: one 16x16 fp32 tile per wave
-    p.lds_tape = p.lds_part + std::max(kMaxItems, kWaves * kTileRows * 16) * 4;
+    p.lds_tape = p.lds_part + std::max(kMaxItems, kWaves * kTileRows * kTileLd) * 4;
     p.lds_bytes = p.lds_tape + p.stages * (int)sizeof(Task);
   };
   lay_out(p.batched ? kRingBatched : kRing);
