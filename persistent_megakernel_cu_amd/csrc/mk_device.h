@@ -833,8 +833,12 @@ __device__ __forceinline__ void gemv_epilogue(const Params& P, Ctx& c, const Tas
     if (w0) st_tag(P.h + addr::layer_off(l, P.F) + pair, sg * v1, tag);
   } else if (OP == OP_LM) {
     if (w0) {
-      c.logits[r] = v0;
-      c.logits[r + 1] = v1;
+      if ((((uintptr_t)(c.logits + r)) & 7u) == 0) {
+        *reinterpret_cast<float2*>(c.logits + r) = make_float2(v0, v1);
+      } else {
+        c.logits[r] = v0;
+        c.logits[r + 1] = v1;
+      }
     }
     if (v0 > best.v) { best.v = v0; best.i = r; }
     if (v1 > best.v) { best.v = v1; best.i = r + 1; }
@@ -1776,6 +1780,22 @@ __device__ __forceinline__ bool gemm_task(const Params& P, Ctx& c, Stream& st, c
           if (live) {
             epi_pair_b<OP>(P, c, l, r, n_col, acc[0], acc[1], rsb);
             epi_pair_b<OP>(P, c, l, r + 2, n_col, acc[2], acc[3], rsb);
+          }
+        } else if (OP == OP_LM) {
+          // the lane's four consecutive logits of its sequence in one store
+          if (live) {
+            const float sc = rsb[n_col];
+            const float4 v = make_float4(acc[0] * sc, acc[1] * sc, acc[2] * sc, acc[3] * sc);
+            float* dst = c.logits + (size_t)n_col * P.V + r;
+            if ((((uintptr_t)dst) & 15u) == 0) {
+              *reinterpret_cast<float4*>(dst) = v;
+            } else {
+              dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+            }
+            if (v.x > best.v) { best.v = v.x; best.i = r; }
+            if (v.y > best.v) { best.v = v.y; best.i = r + 1; }
+            if (v.z > best.v) { best.v = v.z; best.i = r + 2; }
+            if (v.w > best.v) { best.v = v.w; best.i = r + 3; }
           }
         } else {
           if (live) {
