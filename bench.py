@@ -44,20 +44,20 @@ HBM_PEAK_GBPS = 8000.0
 # long-context figure is the mean of its two positions).  They describe the
 # kernel sources whose hash is recorded; any other source gives null.
 MEASURED_TRAFFIC = {
-    "sources_sha256_prefix": "28f9edfff933cbbd",
+    "sources_sha256_prefix": "5ba39d7953320f47",
     "fetch_factor": 2.000,
     "write_factor": 1.000,
     "per_step": {
         "llama1b": {
-            "mega": {"fetch_bytes": 2.5057e9, "write_bytes": 2.320e6},
-            "mega-steps": {"fetch_bytes": 2.5095e9, "write_bytes": 2.324e6},
+            "mega": {"fetch_bytes": 2.5058e9, "write_bytes": 2.319e6},
+            "mega-steps": {"fetch_bytes": 2.5097e9, "write_bytes": 2.323e6},
         },
         "llama1b-long": {
-            "mega": {"fetch_bytes": 2.6961e9, "write_bytes": 7.696e6},
+            "mega": {"fetch_bytes": 2.6962e9, "write_bytes": 7.694e6},
         },
         "llama1b-b8": {
-            "mega": {"fetch_bytes": 2.8203e9, "write_bytes": 2.241e7},
-            "mega-steps": {"fetch_bytes": 2.8198e9, "write_bytes": 2.241e7},
+            "mega": {"fetch_bytes": 2.8192e9, "write_bytes": 2.241e7},
+            "mega-steps": {"fetch_bytes": 2.8189e9, "write_bytes": 2.241e7},
         },
     },
 }

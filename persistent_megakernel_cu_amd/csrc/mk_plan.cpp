@@ -152,12 +152,13 @@ int plan_build(const mk_config& c, int W, Plan& p) {
   int max_res_rows = 0;
   // Which workgroup streams which part of a matrix.  Workgroup b runs on XCD
   // b mod 8.  The gate/up stage streams 256 KB per workgroup (batch 1: 32 row
-  // pairs of 8 KB; batched: 4 blocks of 64 KB); measured on MI355X, the
-  // whole step is 6-8 us faster when workgroup i of the stage takes range
-  // i + 1 (or i + 5) instead of range i, and 7-8 us slower with i + 3 (i + 2,
-  // i + 4, ... change nothing; the same offsets on the other stages change
-  // nothing either): the 256 KB granules of the weight arena are not equally
-  // near to every XCD.
+  // pairs of 8 KB; batched: 4 blocks of 64 KB).  Measured on MI355X with the
+  // batched stage's whole blocks (and the batch-1 stage's whole pairs, before
+  // it took row items), the step is 6-8 us faster when workgroup i of the
+  // stage takes range i + 1 (or i + 5) instead of range i, and 7-8 us slower
+  // with i + 3; even offsets change nothing, nor do offsets of the other
+  // stages or, with row items, any offset at batch 1.  The cause is not
+  // established (a streaming probe shows no XCD-to-address affinity).
   auto range_rotation = [&](Op op, int nw) { return op == OP_GU && nw > 1 ? 1 : 0; };
   // Row pairs of a GEMV stage in contiguous, balanced ranges over workgroups
   // [b0, W), range (i + rotation) mod nw on workgroup b0 + i.
