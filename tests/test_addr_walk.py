@@ -64,6 +64,17 @@ def test_every_index_in_bounds(walk, shape, max_seq, positions):
         assert rep.violations == 0, f"pos {pos}: {rep.first.decode()}"
 
 
+@pytest.mark.parametrize("wgs", [2, 7, 64, 255])
+def test_every_index_in_bounds_on_other_grids(walk, wgs):
+    # fewer workgroups: more row items per wave, and the gate/up ranges'
+    # one-workgroup offset wrapping around a grid that is not a multiple of 8
+    for pos in (0, 47):
+        rc, rep = walk(TINY, 48, pos, num_wgs=wgs)
+        assert rc == mkb.MK_OK, rep.first.decode()
+        assert rep.checks > 0
+        assert rep.violations == 0, f"{wgs} workgroups, pos {pos}: {rep.first.decode()}"
+
+
 @pytest.mark.parametrize("shape,max_seq,pos", [(TINY, 48, 47), (LLAMA_1B, 256, 255), (LLAMA_8B, 2112, 2049)],
                          ids=["tiny", "llama1b", "llama8b"])
 def test_walk_catches_a_one_element_overrun(walk, shape, max_seq, pos):

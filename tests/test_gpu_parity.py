@@ -35,6 +35,15 @@ def test_tiny_chunked_attention(tiny_w):
                        label="tiny-chunks4")
 
 
+@pytest.mark.parametrize("wgs", [7, 64])
+def test_tiny_other_grid_sizes(tiny_w, wgs):
+    # plans over 7 and 64 workgroups: every stage's row items spread over
+    # fewer waves, the gate/up ranges' one-workgroup offset wraps around a
+    # grid that is not a multiple of the XCD count
+    run_teacher_forced(TINY, tiny_w, 48, make_prompt(TINY, 8), 0, 8, mode="mega", num_wgs=wgs,
+                       label=f"tiny-{wgs}wgs")
+
+
 def test_tiny_zero_layers_identity():
     sh = TINY.with_(n_layers=0)
     w = make_weights(sh, master=0)
